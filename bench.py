@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X NT GEMM on its headline workload.
+
+One step = one call of the library (C = A . B^T) on one set of synthetic inputs
+that are already resident in HBM.  Input sets rotate so the 256 MB last-level
+cache cannot hold them across steps (cold-cache numbers).  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--quick]
+
+Primary workload: M = N = K = 4096, BF16 inputs uniform on [-1, 1), FP32
+accumulation, BF16 output.  A second line item in the same JSON object reports
+the decode-regime shape M = 256, N = 28672, K = 8192 (A ~ N(0,1), B ~ N(0, 0.02^2)).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2500.0     # MI355X dense BF16/FP16 MFMA, published
+HBM_TBS = 8.0            # MI355X HBM3E, published
+KERNEL_SOURCES = [os.path.join(ROOT, "dense_gemm_nt_amd", "csrc", f)
+                  for f in ("gemm_nt_kernel.hpp", "gemm_nt.hip")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the kernel as it is now (same source hash); else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload_key)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_gemm(g, shapes, steps, warmup, sets, in_dt, out_dt, dist):
+    import torch
+    from gemm_inputs import make_operands
+    M, N, K = shapes
+    dev = torch.device("cuda", 0)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+    code = {"bf16": 0, "fp16": 1, "fp32": 2}
+    bufs = []
+    for i in range(sets):
+        A, B = make_operands(M, N, K, in_dt, dist, seed=i)
+        bufs.append((A.to(dev), B.to(dev), torch.empty((M, N), dtype=tdt[out_dt], device=dev)))
+        del A, B
+    h = g.Gemm()
+    stream = torch.cuda.Stream(device=dev)
+    sp = stream.cuda_stream
+
+    def launch(i):
+        A, B, C = bufs[i % sets]
+        h.run_raw(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, K, K, N,
+                  code[in_dt], code[out_dt], sp)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            launch(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / steps
+    event_ms = ev0.elapsed_time(ev1) / steps
+    # the output of the last step, for a parity spot check
+    last = (steps - 1) % sets
+    h.close()
+    return wall_ms, event_ms, bufs, last
+
+
+def spot_check(bufs, idx, shapes, in_dt, out_dt, dist):
+    """Oracle on two rows and 2000 points of the last timed output."""
+    import numpy as np
+    import oracle
+    from gemm_inputs import make_operands
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from tests.tolerance import check
+    M, N, K = shapes
+    A, B = make_operands(M, N, K, in_dt, dist, seed=idx)
+    C = bufs[idx][2].float().cpu().double().numpy()
+    rows = [0, M - 1]
+    Cr, S = oracle.gemm_nt_rows(A, B, rows, K=K, in_dtype=in_dt)
+    e1, w1 = check(C[rows], Cr, S, out_dt, "bench rows")
+    rng = np.random.default_rng(1)
+    ii, jj = rng.integers(0, M, 2000), rng.integers(0, N, 2000)
+    Cp, Sp = oracle.gemm_nt_points(A, B, ii, jj, K=K, in_dtype=in_dt)
+    e2, w2 = check(C[ii, jj], Cp, Sp, out_dt, "bench points")
+    return max(w1, w2)
+
+
+def cpu_baseline(shapes, in_dt, dist, target_s=10.0):
+    """The oracle as it is, on whole rows of the same workload, on this host's cores."""
+    import oracle
+    from gemm_inputs import make_operands
+    M, N, K = shapes
+    A, B = make_operands(M, N, K, in_dt, dist, seed=0)
+    rows = 16
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_nt_rows(A, B, list(range(rows)), K=K, in_dtype=in_dt)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or rows >= M:
+            break
+        rows = min(M, max(rows * 2, int(rows * target_s / max(dt, 1e-3) * 1.1)))
+    flops = 2.0 * rows * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d output rows of the %dx%dx%d product (%.1f GFLOP) in %.1f s"
+                      % (rows, M, M, N, K, flops / 1e9, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-check", action="store_true", help="skip the parity spot check")
+    ap.add_argument("--quick", action="store_true", help="primary workload only")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GEMM has no multi-GPU path here "
+              "(rerun with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_gemm_nt_amd as g
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    from dense_gemm_nt_amd import roofline
+
+    # primary: 4096^3 bf16 -> bf16, six rotating input sets (6 x 96 MB > 256 MB cache)
+    shapes = (4096, 4096, 4096)
+    wall_ms, event_ms, bufs, last = time_gemm(g, shapes, args.steps, args.warmup, 6,
+                                              "bf16", "bf16", "uniform")
+    worst = None if args.no_check else spot_check(bufs, last, shapes, "bf16", "bf16", "uniform")
+    del bufs
+    torch.cuda.empty_cache()
+    M, N, K = shapes
+    flops = 2.0 * M * N * K
+    plan = g.gemm_plan(M, N, K, 0, 0)
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (event_ms * 1e-3) / 1e12
+    out = {
+        "metric": "TFLOP/s & % MFMA peak, BF16 GEMM at 4096^3 and 256x28672x8192",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: A, B uniform[-1,1) rounded to bf16, seeds 0..5 rotating",
+        "config": {"workload": "gemm_nt M=N=K=4096 bf16 in, fp32 accumulate, bf16 out",
+                   "M": M, "N": N, "K": K, "plan": plan["name"],
+                   "pct_mfma_peak": round(100 * value / PEAK_TFLOPS, 2),
+                   "cache": "cold: 6 rotating input sets (576 MB)",
+                   "parity_worst_err_over_bound": worst},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": traffic_for("4096^3 bf16->bf16"),
+                     "kernel_avg_us": round(event_ms * 1e3, 3)},
+    }
+
+    if not args.quick:
+        # decode-regime shape from the same metric: HBM-bound on this machine
+        d = (256, 28672, 8192)
+        w2, e2, bufs, last = time_gemm(g, d, max(20, args.steps // 2), args.warmup, 2,
+                                       "bf16", "bf16", "llm")
+        worst2 = None if args.no_check else spot_check(bufs, last, d, "bf16", "bf16", "llm")
+        del bufs
+        torch.cuda.empty_cache()
+        r = roofline.roofline(*d, 2, 2, peak_tflops=PEAK_TFLOPS, hbm_tbs=HBM_TBS)
+        tf = 2.0 * d[0] * d[1] * d[2] / (e2 * 1e-3) / 1e12
+        gbs = r.bytes / (e2 * 1e-3) / 1e9
+        out["secondary"] = {
+            "workload": "gemm_nt M=256 N=28672 K=8192 bf16->bf16 (decode MLP-up)",
+            "plan": g.gemm_plan(*d, 0, 0)["name"],
+            "splits": g.gemm_plan(*d, 0, 0)["splits"],
+            "ms_per_step": round(w2, 5),
+            "tflops": round(2.0 * d[0] * d[1] * d[2] / (w2 * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_TBS * 1000,
+                         "unit": "GB/s", "frac": round(gbs / (HBM_TBS * 1000), 4),
+                         "kernel_avg_us": round(e2 * 1e3, 3), "kernel_tflops": round(tf, 2),
+                         "traffic": traffic_for("256x28672x8192 bf16->bf16")},
+            "parity_worst_err_over_bound": worst2,
+        }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(shapes, "bf16", "uniform")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,99 @@
+"""ctypes binding of the C ABI in include/gemm_nt.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgemm_nt.so")
+
+GEMM_BF16, GEMM_FP16, GEMM_FP32 = 0, 1, 2
+GEMM_OK = 0
+STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_UNSUPPORTED",
+          3: "GEMM_ERR_MISALIGNED", 4: "GEMM_ERR_ALLOC", 5: "GEMM_ERR_HIP"}
+
+# Every symbol include/gemm_nt.h declares.
+EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_validate", "gemm_plan",
+           "gemm_status_string")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__("%s%s" % (STATUS.get(status, "status %d" % status),
+                                   (": " + what) if what else ""))
+
+
+class GemmPlan(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("block_k", ctypes.c_int),
+                ("waves", ctypes.c_int), ("stages", ctypes.c_int), ("splits", ctypes.c_int),
+                ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64), ("name", ctypes.c_char * 48)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["name"] = self.name.decode()
+        return d
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgemm_nt.so is not built; run `python -m dense_gemm_nt_amd.build` "
+                           "or __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.gemm_create.argtypes = [ctypes.POINTER(vp)]
+    L.gemm_create.restype = ci
+    L.gemm_destroy.argtypes = [vp]
+    L.gemm_destroy.restype = ci
+    L.gemm_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    L.gemm_run.restype = ci
+    L.gemm_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci]
+    L.gemm_validate.restype = ci
+    L.gemm_plan.argtypes = [i64, i64, i64, ci, ci, ctypes.POINTER(GemmPlan)]
+    L.gemm_plan.restype = ci
+    L.gemm_status_string.argtypes = [ci]
+    L.gemm_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def check(status, what=""):
+    if status != GEMM_OK:
+        raise GemmError(status, what)
+
+
+def gemm_create():
+    h = ctypes.c_void_p()
+    check(lib().gemm_create(ctypes.byref(h)), "gemm_create")
+    return h
+
+
+def gemm_destroy(h):
+    check(lib().gemm_destroy(h), "gemm_destroy")
+
+
+def gemm_run(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, stream):
+    """Raw entry point: A, B, C and stream are integer device addresses / a hipStream_t."""
+    return lib().gemm_run(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, stream)
+
+
+def gemm_validate(A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype):
+    return lib().gemm_validate(A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype)
+
+
+def gemm_plan(M, N, K, in_dtype=GEMM_BF16, out_dtype=GEMM_BF16):
+    p = GemmPlan()
+    check(lib().gemm_plan(M, N, K, in_dtype, out_dtype, ctypes.byref(p)), "gemm_plan")
+    return p.as_dict()
+
+
+def gemm_status_string(s):
+    return lib().gemm_status_string(s).decode()

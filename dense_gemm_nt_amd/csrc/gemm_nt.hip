@@ -1,0 +1,354 @@
+// gemm_nt.hip -- host side of the NT GEMM library: the C ABI declared in
+// include/gemm_nt.h, argument checks, the per-shape plan and the launches.
+//
+// Planning follows "A Blackwell GEMM by Hand in CuTe DSL", section 1 (M decides
+// the regime; the number of tiles against the number of compute units decides
+// decode performance) and section 9 (smaller N tiles and split-K for decode;
+// libraries ship a family of kernels and pick per shape).  Here the family is a
+// handful of tile shapes of one kernel template; a shape picks its tile by M
+// and then splits K until the grid covers the 256 compute units.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "gemm_nt.h"
+#include "gemm_nt_kernel.hpp"
+
+namespace {
+
+using gnt::KernelArgs;
+
+constexpr int kNumCUs = 256;
+constexpr int64_t kMaxLeadingDim = (int64_t)1 << 22;   // keeps tile byte offsets below 2^31
+constexpr int64_t kDefaultWorkspaceMB = 64;
+constexpr int kMaxCounters = 1 << 16;
+
+typedef hipError_t (*launch_fn)(const KernelArgs &, unsigned grid, hipStream_t);
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, int IN, int OUT, bool KMASK>
+hipError_t launch_cfg(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gnt::gemm_nt_kernel<BM, BN, BK, WM, WN, ST, IN, OUT, KMASK>), dim3(grid),
+                       dim3(WM * WN * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+struct Config {
+    const char *name;
+    int bm, bn, bk, wm, wn, stages;
+    int kmask;
+    launch_fn fn[2][3];   // [in dtype][out dtype]
+};
+
+#define GNT_FNS(BM, BN, BK, WM, WN, ST, KM)                                                      \
+    {                                                                                            \
+        {launch_cfg<BM, BN, BK, WM, WN, ST, 0, 0, KM>, launch_cfg<BM, BN, BK, WM, WN, ST, 0, 1, KM>, \
+         launch_cfg<BM, BN, BK, WM, WN, ST, 0, 2, KM>},                                          \
+        {launch_cfg<BM, BN, BK, WM, WN, ST, 1, 0, KM>, launch_cfg<BM, BN, BK, WM, WN, ST, 1, 1, KM>, \
+         launch_cfg<BM, BN, BK, WM, WN, ST, 1, 2, KM>},                                          \
+    }
+
+// The kernel family.  LDS per workgroup = stages * (BM + BN) * BK * 2 bytes, at
+// most 160 KB; each wave owns a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
+// Configurations with kmask = 1 zero the operand columns past K in registers and
+// are the only ones planned when K is not a multiple of 8.
+const Config kConfigs[] = {
+    {"256x256x64_w4_s2", 256, 256, 64, 2, 2, 2, 0, GNT_FNS(256, 256, 64, 2, 2, 2, false)},
+    {"256x128x64_w4_s3", 256, 128, 64, 2, 2, 3, 0, GNT_FNS(256, 128, 64, 2, 2, 3, false)},
+    {"128x128x64_w4_s4", 128, 128, 64, 2, 2, 4, 0, GNT_FNS(128, 128, 64, 2, 2, 4, false)},
+    {"32x256x64_w4_s4", 32, 256, 64, 1, 4, 4, 0, GNT_FNS(32, 256, 64, 1, 4, 4, false)},
+    {"128x128x64_w4_s4_kmask", 128, 128, 64, 2, 2, 4, 1, GNT_FNS(128, 128, 64, 2, 2, 4, true)},
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+struct Plan {
+    int cfg;
+    int tiles_m, tiles_n;
+    int k_tiles;
+    int splits;
+    int kt_per_split;
+    int group_m;
+    int64_t grid;
+    int64_t ws_bytes;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int find_config(const char *name)
+{
+    for (int i = 0; i < kNumConfigs; ++i)
+        if (strcmp(kConfigs[i].name, name) == 0)
+            return i;
+    return -1;
+}
+
+// Pick the tile shape and the K split for a problem.  `ws_bytes` bounds the
+// split-K partial storage; `force_cfg` / `force_splits` (>= 0 / > 0) override.
+Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg, int force_splits)
+{
+    Plan p{};
+    int cfg;
+    if (force_cfg >= 0) {
+        cfg = force_cfg;
+    } else if (K % 8) {
+        cfg = 4;
+    } else if (M <= 32) {
+        cfg = 3;
+    } else if (M <= 128) {
+        cfg = 2;
+    } else if (M <= 256) {
+        cfg = 1;
+    } else {
+        const int64_t big = cdiv(M, 256) * cdiv(N, 256);
+        cfg = big >= 128 ? 0 : 2;
+    }
+    if ((K % 8) && !kConfigs[cfg].kmask)
+        cfg = 4;
+    const Config &c = kConfigs[cfg];
+    p.cfg = cfg;
+    p.tiles_m = (int)cdiv(M, c.bm);
+    p.tiles_n = (int)cdiv(N, c.bn);
+    p.k_tiles = (int)cdiv(K, c.bk);
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t tile_bytes = (int64_t)c.bm * c.bn * 4;
+
+    int splits = 1;
+    if (force_splits > 0) {
+        splits = force_splits;
+    } else if (tiles < kNumCUs && p.k_tiles >= 16) {
+        // Fill the compute units, keeping at least 8 k-slabs per split.
+        splits = (int)(kNumCUs / tiles);
+        if (splits > p.k_tiles / 8)
+            splits = p.k_tiles / 8;
+        if (splits < 1)
+            splits = 1;
+    }
+    if (splits > 1 && tiles > kMaxCounters)
+        splits = 1;
+    while (splits > 1 && tiles * splits * tile_bytes > ws_bytes)
+        --splits;
+    if (p.k_tiles == 0)
+        splits = 1;
+    if (splits > p.k_tiles && p.k_tiles > 0)
+        splits = p.k_tiles;
+    p.kt_per_split = splits > 1 ? (int)cdiv(p.k_tiles, splits) : p.k_tiles;
+    if (splits > 1)
+        splits = (int)cdiv(p.k_tiles, p.kt_per_split);   // no empty split
+    p.splits = splits;
+    p.group_m = p.tiles_m >= 4 ? 4 : p.tiles_m;
+    if (p.group_m < 1)
+        p.group_m = 1;
+    p.grid = tiles * splits;
+    p.ws_bytes = splits > 1 ? tiles * splits * tile_bytes : 0;
+    return p;
+}
+
+}  // namespace
+
+struct gemm_handle_s {
+    int device;
+    float *partials;
+    unsigned *counters;
+    int64_t ws_bytes;
+    int force_cfg;
+    int force_splits;
+    int log;
+};
+
+extern "C" {
+
+const char *gemm_status_string(int s)
+{
+    switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+    case GEMM_ERR_MISALIGNED: return "GEMM_ERR_MISALIGNED";
+    case GEMM_ERR_ALLOC: return "GEMM_ERR_ALLOC";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    default: return "GEMM_ERR_UNKNOWN";
+    }
+}
+
+gemm_status_t gemm_validate(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                            int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype)
+{
+    if (in_dtype != GEMM_BF16 && in_dtype != GEMM_FP16)
+        return GEMM_ERR_UNSUPPORTED;
+    if (out_dtype != GEMM_BF16 && out_dtype != GEMM_FP16 && out_dtype != GEMM_FP32)
+        return GEMM_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_ERR_INVALID_ARG;
+    if (lda < K || ldb < K || ldc < N || lda < 0 || ldb < 0)
+        return GEMM_ERR_INVALID_ARG;
+    if (M >= INT32_MAX || N >= INT32_MAX || K >= INT32_MAX || ldc >= INT32_MAX)
+        return GEMM_ERR_UNSUPPORTED;
+    if (lda >= kMaxLeadingDim || ldb >= kMaxLeadingDim)
+        return GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if (!C)
+        return GEMM_ERR_INVALID_ARG;
+    const uintptr_t out_size = out_dtype == GEMM_FP32 ? 4 : 2;
+    if ((uintptr_t)C % out_size)
+        return GEMM_ERR_MISALIGNED;
+    if (K == 0)
+        return GEMM_OK;
+    if (!A || !B)
+        return GEMM_ERR_INVALID_ARG;
+    if ((uintptr_t)A % 16 || (uintptr_t)B % 16 || lda % 8 || ldb % 8)
+        return GEMM_ERR_MISALIGNED;
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, gemm_plan_t *out)
+{
+    if (!out)
+        return GEMM_ERR_INVALID_ARG;
+    memset(out, 0, sizeof(*out));
+    if (in_dtype != GEMM_BF16 && in_dtype != GEMM_FP16)
+        return GEMM_ERR_UNSUPPORTED;
+    if (out_dtype != GEMM_BF16 && out_dtype != GEMM_FP16 && out_dtype != GEMM_FP32)
+        return GEMM_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_ERR_INVALID_ARG;
+    if (M >= INT32_MAX || N >= INT32_MAX || K >= INT32_MAX)
+        return GEMM_ERR_UNSUPPORTED;
+    const Plan p = make_plan(M, N, K, kDefaultWorkspaceMB << 20, -1, -1);
+    const Config &c = kConfigs[p.cfg];
+    out->block_m = c.bm;
+    out->block_n = c.bn;
+    out->block_k = c.bk;
+    out->waves = c.wm * c.wn;
+    out->stages = c.stages;
+    out->splits = p.splits;
+    out->tiles = (int64_t)p.tiles_m * p.tiles_n;
+    out->workgroups = (M == 0 || N == 0) ? 0 : p.grid;
+    out->workspace_bytes = p.ws_bytes;
+    snprintf(out->name, sizeof(out->name), "%s", c.name);
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_create(gemm_handle_t *out)
+{
+    if (!out)
+        return GEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    gemm_handle_s *h = new (std::nothrow) gemm_handle_s{};
+    if (!h)
+        return GEMM_ERR_ALLOC;
+    h->force_cfg = -1;
+    h->force_splits = -1;
+    int64_t mb = kDefaultWorkspaceMB;
+    if (const char *e = getenv("GEMM_WORKSPACE_MB"))
+        mb = atoll(e) > 0 ? atoll(e) : mb;
+    if (const char *e = getenv("GEMM_CONFIG"))
+        h->force_cfg = find_config(e);
+    if (const char *e = getenv("GEMM_SPLITS"))
+        h->force_splits = atoi(e);
+    if (const char *e = getenv("GEMM_LOG"))
+        h->log = atoi(e);
+    h->ws_bytes = mb << 20;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return GEMM_ERR_HIP;
+    }
+    if (const char *e = getenv("GEMM_TEST_FAIL_ALLOC")) {
+        if (atoi(e)) {
+            delete h;
+            return GEMM_ERR_ALLOC;
+        }
+    }
+    if (hipMalloc(&h->partials, (size_t)h->ws_bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return GEMM_ERR_ALLOC;
+    }
+    if (hipMalloc(&h->counters, sizeof(unsigned) * kMaxCounters) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(h->partials);
+        delete h;
+        return GEMM_ERR_ALLOC;
+    }
+    if (hipMemset(h->counters, 0, sizeof(unsigned) * kMaxCounters) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->partials);
+        (void)hipFree(h->counters);
+        delete h;
+        return GEMM_ERR_HIP;
+    }
+    *out = h;
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_destroy(gemm_handle_t h)
+{
+    if (!h)
+        return GEMM_OK;
+    gemm_status_t st = GEMM_OK;
+    if (hipFree(h->partials) != hipSuccess)
+        st = GEMM_ERR_HIP;
+    if (hipFree(h->counters) != hipSuccess)
+        st = GEMM_ERR_HIP;
+    delete h;
+    return st;
+}
+
+gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, int64_t M, int64_t N,
+                       int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype,
+                       hipStream_t stream)
+{
+    if (!h)
+        return GEMM_ERR_INVALID_ARG;
+    gemm_status_t st = gemm_validate(A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype);
+    if (st != GEMM_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GEMM_ERR_HIP;
+    if (dev != h->device)
+        return GEMM_ERR_INVALID_ARG;
+
+    const Plan p = make_plan(M, N, K, h->ws_bytes, h->force_cfg, h->force_splits);
+    if (p.splits > 1 && (p.ws_bytes > h->ws_bytes || (int64_t)p.tiles_m * p.tiles_n > kMaxCounters))
+        return GEMM_ERR_UNSUPPORTED;
+    if (p.grid <= 0 || p.grid >= INT32_MAX)
+        return GEMM_ERR_UNSUPPORTED;
+    const Config &c = kConfigs[p.cfg];
+
+    KernelArgs a{};
+    a.A = static_cast<const uint16_t *>(A);
+    a.B = static_cast<const uint16_t *>(B);
+    a.C = C;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.lda = (int)lda;
+    a.ldb = (int)ldb;
+    a.ldc = (int)ldc;
+    a.tiles_m = p.tiles_m;
+    a.tiles_n = p.tiles_n;
+    a.k_tiles = p.k_tiles;
+    a.splits = p.splits;
+    a.kt_per_split = p.kt_per_split;
+    a.group_m = p.group_m;
+    const uintptr_t vec_bytes = out_dtype == GEMM_FP32 ? 16 : 8;
+    a.vec_store = (ldc % 4 == 0) && ((uintptr_t)C % vec_bytes == 0);
+    a.partials = h->partials;
+    a.counters = h->counters;
+    if (h->log)
+        fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld\n",
+                (long long)M, (long long)N, (long long)K, c.name, p.tiles_m, p.tiles_n, p.splits,
+                p.kt_per_split, (long long)p.grid);
+    const hipError_t e = c.fn[in_dtype][out_dtype](a, (unsigned)p.grid, stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // extern "C"

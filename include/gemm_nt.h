@@ -1,0 +1,105 @@
+/*
+ * gemm_nt.h -- C ABI of the MI355X (gfx950) NT GEMM library.
+ *
+ * Operation (all three pages that write the kernel out agree on it):
+ *   C[i, j] = out( sum_{k=0}^{K-1} A[i, k] * B[j, k] ),   0 <= i < M, 0 <= j < N
+ * "A Blackwell GEMM by Hand in CuTe DSL: TMA, mbarriers, TMEM, and tcgen05",
+ * section 1 (C = A . B^T, 2MNK operations) and section 3 (A and B both K-major,
+ * 16-bit inputs, FP32 accumulation); "Matmul on sm_120", The tiled view (the
+ * per-element sum, and the tiled form the kernels compute it in).
+ *
+ * Storage: row-major with element strides.  A is M rows of lda elements, B is N
+ * rows of ldb elements (the [out, in] weight layout of a linear layer), C is M
+ * rows of ldc elements; only the first K columns of A and B and the first N
+ * columns of C are touched.  Inputs are both BF16 or both FP16; products are
+ * exact and accumulate in FP32; the FP32 sum is written as FP32 or rounded to
+ * BF16/FP16 with round-to-nearest-even.  The summation order is unspecified
+ * (any order the tiling chooses), but for given arguments every call on the
+ * same device returns the same bits.
+ *
+ * Ownership: A, B and C are device pointers owned by the caller.  The handle
+ * owns its workspace (split-K partial tiles and per-tile counters).
+ *
+ * Streams: gemm_run only enqueues work on `stream` (0 = the null stream) and
+ * never synchronises.  One handle must not be used by two calls that may run
+ * concurrently (its workspace is shared); use one handle per stream.
+ *
+ * Errors: every argument error is returned before any device work is enqueued.
+ */
+#ifndef GEMM_NT_H
+#define GEMM_NT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+typedef struct gemm_handle_s *gemm_handle_t;
+
+typedef enum {
+    GEMM_BF16 = 0,
+    GEMM_FP16 = 1,
+    GEMM_FP32 = 2
+} gemm_dtype_t;
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1, /* null pointer, negative size, leading dimension too small */
+    GEMM_ERR_UNSUPPORTED = 2, /* unknown dtype enum, FP32 inputs, a size beyond the limits */
+    GEMM_ERR_MISALIGNED = 3,  /* A/B base or row pitch not a multiple of 16 bytes */
+    GEMM_ERR_ALLOC = 4,       /* workspace allocation failed */
+    GEMM_ERR_HIP = 5          /* a HIP runtime call or a launch failed */
+} gemm_status_t;
+
+/* Create a handle on the current device: allocates the split-K workspace and
+ * zeroes its per-tile counters (synchronously).  *out is set to NULL on error. */
+gemm_status_t gemm_create(gemm_handle_t *out);
+
+/* C = A . B^T (see the top of this file).
+ *   A, B      device pointers, 16-byte aligned; lda, ldb multiples of 8 elements
+ *   C         device pointer, any alignment of its element type; ldc >= N
+ *   M, N, K   >= 0; M = 0 or N = 0 enqueues nothing; K = 0 writes zeros
+ *   lda >= K, ldb >= K, ldc >= N (elements); lda and ldb below 2^22
+ *   in_dtype  GEMM_BF16 or GEMM_FP16 (both operands)
+ *   out_dtype GEMM_BF16, GEMM_FP16 or GEMM_FP32
+ * Returns GEMM_OK after enqueueing, or an error status with nothing enqueued. */
+gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C,
+                       int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                       int in_dtype, int out_dtype, hipStream_t stream);
+
+/* Release the handle and its workspace.  NULL is a no-op.  The caller must make
+ * sure no call enqueued with this handle is still running. */
+gemm_status_t gemm_destroy(gemm_handle_t h);
+
+/* Host-only argument check that gemm_run performs first (no device access). */
+gemm_status_t gemm_validate(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                            int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int in_dtype,
+                            int out_dtype);
+
+/* The kernel configuration gemm_run would launch for a shape (host only). */
+typedef struct {
+    int block_m, block_n, block_k; /* output tile and K depth of one LDS stage */
+    int waves;                     /* wavefronts per workgroup */
+    int stages;                    /* LDS ring depth */
+    int splits;                    /* K splits per output tile (1 = none) */
+    int64_t tiles;                 /* output tiles */
+    int64_t workgroups;            /* grid size */
+    int64_t workspace_bytes;       /* split-K partials used */
+    char name[48];                 /* kernel configuration name */
+} gemm_plan_t;
+
+gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+                        gemm_plan_t *plan);
+
+/* Human-readable name of a status code (static storage). */
+const char *gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_NT_H */

@@ -190,10 +190,12 @@ int oracle_gemm_nt_rows(const uint16_t *A, const uint16_t *B, int64_t M, int64_t
         free(table);
         return -1;
     }
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t r = 0; r < nrows; ++r) {
-        const int64_t i = rows[r];
-        for (int64_t j = 0; j < N; ++j) {
+    /* Columns outermost so each row of B is streamed from memory once for all
+     * the selected rows; every element is still one dot_one() in k order. */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < N; ++j) {
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t i = rows[r];
             double c, s;
             dot_one(table, A + i * lda, B + j * ldb, K, &c, &s);
             C[r * N + j] = c;

@@ -1,0 +1,118 @@
+"""The C-ABI library on the host: it loads, exports what the header declares, and
+its argument checks and plans behave as documented.  No device work here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_nt.h")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import dense_gemm_nt_amd as g
+    from dense_gemm_nt_amd import build
+    if build.stale():
+        build.build()
+    return g
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(g):
+    from dense_gemm_nt_amd import _lib
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    L = _lib.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(_lib.EXPORTS) == declared
+
+
+def test_status_strings(g):
+    assert g.gemm_status_string(0) == "GEMM_OK"
+    assert g.gemm_status_string(3) == "GEMM_ERR_MISALIGNED"
+    assert g.gemm_status_string(99) == "GEMM_ERR_UNKNOWN"
+
+
+A16 = 0x10000          # a 16-byte aligned fake address (never dereferenced)
+
+
+@pytest.mark.parametrize("args,want", [
+    # (A, B, C, M, N, K, lda, ldb, ldc, in, out)
+    ((A16, A16, A16, 4, 4, 8, 8, 8, 4, 0, 0), 0),
+    ((A16, A16, A16, 4, 4, 8, 8, 8, 4, 1, 2), 0),
+    ((A16, A16, A16, 4, 4, 8, 8, 8, 4, 2, 0), 2),     # fp32 inputs unsupported
+    ((A16, A16, A16, 4, 4, 8, 8, 8, 4, 0, 7), 2),     # unknown output enum
+    ((A16, A16, A16, -1, 4, 8, 8, 8, 4, 0, 0), 1),    # negative M
+    ((A16, A16, A16, 4, 4, 8, 7, 8, 4, 0, 0), 1),     # lda < K
+    ((A16, A16, A16, 4, 4, 8, 8, 8, 3, 0, 0), 1),     # ldc < N
+    ((0, A16, A16, 4, 4, 8, 8, 8, 4, 0, 0), 1),       # null A
+    ((A16, A16, 0, 4, 4, 8, 8, 8, 4, 0, 0), 1),       # null C
+    ((A16 + 2, A16, A16, 4, 4, 8, 8, 8, 4, 0, 0), 3),  # A not 16-byte aligned
+    ((A16, A16, A16, 4, 4, 8, 12, 8, 4, 0, 0), 3),    # lda not a multiple of 8
+    ((A16, A16, A16 + 2, 4, 4, 8, 8, 8, 4, 0, 2), 3),  # fp32 C not 4-byte aligned
+    ((A16, A16, A16 + 2, 4, 4, 8, 8, 8, 4, 0, 0), 0),  # bf16 C needs only 2 bytes
+    ((0, 0, 0, 0, 4, 8, 8, 8, 4, 0, 0), 0),           # M = 0: nothing to do
+    ((0, 0, A16, 4, 4, 0, 0, 0, 4, 0, 0), 0),         # K = 0: zeros, A/B unused
+    ((A16, A16, A16, 4, 4, 8, 1 << 22, 8, 4, 0, 0), 2),  # lda beyond the limit
+])
+def test_validate(g, args, want):
+    assert g.gemm_validate(*args) == want
+
+
+def test_run_rejects_null_handle_before_any_device_work(g):
+    from dense_gemm_nt_amd import _lib
+    st = _lib.lib().gemm_run(None, A16, A16, A16, 4, 4, 8, 8, 8, 4, 0, 0, None)
+    assert st == 1
+
+
+def test_destroy_null_is_noop(g):
+    from dense_gemm_nt_amd import _lib
+    assert _lib.lib().gemm_destroy(None) == 0
+
+
+def test_create_rejects_null_out(g):
+    from dense_gemm_nt_amd import _lib
+    assert _lib.lib().gemm_create(None) == 1
+
+
+LDS_BYTES = 160 * 1024
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (512, 512, 512), (4096, 4096, 4096), (8192, 8192, 8192), (8192, 28672, 8192),
+    (256, 28672, 8192), (256, 8192, 28672), (256, 10240, 8192), (256, 8192, 8192),
+    (1000, 4097, 1536), (127, 28672, 8192), (3000, 3000, 5000), (1, 8192, 8192),
+    (5, 7, 37), (33, 65, 1),
+])
+def test_plans_fit_the_machine(g, M, N, K):
+    p = g.gemm_plan(M, N, K, 0, 0)
+    bm, bn, bk = p["block_m"], p["block_n"], p["block_k"]
+    assert p["stages"] * (bm + bn) * bk * 2 <= LDS_BYTES
+    assert p["tiles"] == -(-M // bm) * -(-N // bn)
+    assert p["workgroups"] == p["tiles"] * p["splits"]
+    k_tiles = -(-K // bk)
+    assert 1 <= p["splits"] <= max(1, k_tiles)
+    if p["splits"] > 1:
+        assert p["workspace_bytes"] == p["tiles"] * p["splits"] * bm * bn * 4
+        assert p["workspace_bytes"] <= 64 << 20
+    else:
+        assert p["workspace_bytes"] == 0
+    if K % 8:
+        assert p["name"].endswith("kmask")
+
+
+def test_plan_regimes(g):
+    # prefill / square: the big tile, one or more full waves of 256 CUs
+    assert g.gemm_plan(4096, 4096, 4096)["tiles"] == 256
+    assert g.gemm_plan(8192, 8192, 8192)["tiles"] == 1024
+    # decode with few tiles splits K to cover the compute units
+    p = g.gemm_plan(256, 8192, 8192)
+    assert p["splits"] > 1 and p["workgroups"] >= 128
