@@ -18,6 +18,7 @@
 
 #include "gemm_nt.h"
 #include "gemm_nt_kernel.hpp"
+#include "gemm_nt_pingpong.hpp"
 
 namespace {
 
@@ -25,8 +26,7 @@ using gnt::KernelArgs;
 
 constexpr int kNumCUs = 256;
 constexpr int64_t kMaxLeadingDim = (int64_t)1 << 22;   // keeps tile byte offsets below 2^31
-constexpr int64_t kDefaultWorkspaceMB = 64;
-constexpr int kMaxCounters = 1 << 16;
+constexpr int64_t kDefaultWorkspaceMB = 128;
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, unsigned grid, hipStream_t);
 
@@ -38,10 +38,39 @@ hipError_t launch_cfg(const KernelArgs &a, unsigned grid, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int IN, int OUT, int BK, int S, int PF>
+hipError_t launch_pingpong(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gnt::gemm_nt_pingpong<IN, OUT, BK, S, PF>), dim3(grid), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+#define GNT_PP(BK, S, PF)                                                                        \
+    {                                                                                            \
+        {launch_pingpong<0, 0, BK, S, PF>, launch_pingpong<0, 1, BK, S, PF>,                     \
+         launch_pingpong<0, 2, BK, S, PF>},                                                      \
+        {launch_pingpong<1, 0, BK, S, PF>, launch_pingpong<1, 1, BK, S, PF>,                     \
+         launch_pingpong<1, 2, BK, S, PF>},                                                      \
+    }
+
+hipError_t launch_splitk_sum(const KernelArgs &a, int out_dtype, hipStream_t s)
+{
+    const int64_t threads = (int64_t)a.M * ((a.N + 3) / 4);
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    if (out_dtype == GEMM_BF16)
+        hipLaunchKernelGGL(gnt::splitk_sum<gnt::OUT_BF16>, dim3(grid), dim3(256), 0, s, a);
+    else if (out_dtype == GEMM_FP16)
+        hipLaunchKernelGGL(gnt::splitk_sum<gnt::OUT_FP16>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(gnt::splitk_sum<gnt::OUT_FP32>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 struct Config {
     const char *name;
-    int bm, bn, bk, wm, wn, stages;
-    int kmask;
+    int bm, bn, bk, waves, stages;
+    int kmask;      // zeroes operand columns past K in registers (any K)
+    int splitk;     // supports splits > 1
     launch_fn fn[2][3];   // [in dtype][out dtype]
 };
 
@@ -58,13 +87,23 @@ struct Config {
 // Configurations with kmask = 1 zero the operand columns past K in registers and
 // are the only ones planned when K is not a multiple of 8.
 const Config kConfigs[] = {
-    {"256x256x64_w4_s2", 256, 256, 64, 2, 2, 2, 0, GNT_FNS(256, 256, 64, 2, 2, 2, false)},
-    {"256x128x64_w4_s3", 256, 128, 64, 2, 2, 3, 0, GNT_FNS(256, 128, 64, 2, 2, 3, false)},
-    {"128x128x64_w4_s4", 128, 128, 64, 2, 2, 4, 0, GNT_FNS(128, 128, 64, 2, 2, 4, false)},
-    {"32x256x64_w4_s4", 32, 256, 64, 1, 4, 4, 0, GNT_FNS(32, 256, 64, 1, 4, 4, false)},
-    {"128x128x64_w4_s4_kmask", 128, 128, 64, 2, 2, 4, 1, GNT_FNS(128, 128, 64, 2, 2, 4, true)},
+    {"256x256x64_w4_s2", 256, 256, 64, 4, 2, 0, 1, GNT_FNS(256, 256, 64, 2, 2, 2, false)},
+    {"256x128x64_w4_s3", 256, 128, 64, 4, 3, 0, 1, GNT_FNS(256, 128, 64, 2, 2, 3, false)},
+    {"128x128x64_w4_s4", 128, 128, 64, 4, 4, 0, 1, GNT_FNS(128, 128, 64, 2, 2, 4, false)},
+    {"32x256x64_w4_s4", 32, 256, 64, 4, 4, 0, 1, GNT_FNS(32, 256, 64, 1, 4, 4, false)},
+    {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 1, 1, GNT_FNS(128, 128, 64, 2, 2, 4, true)},
+    {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 0, 1, GNT_PP(64, 2, 0)},
+    {"256x256x32_w8_pingpong_s5", 256, 256, 32, 8, 5, 0, 1, GNT_PP(32, 5, 0)},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+enum {
+    CFG_W4_256x256 = 0,
+    CFG_W4_256x128 = 1,
+    CFG_W4_128x128 = 2,
+    CFG_W4_32x256 = 3,
+    CFG_W4_128x128_KMASK = 4,
+    CFG_PP_256x256 = 5,
+};
 
 struct Plan {
     int cfg;
@@ -96,29 +135,34 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     if (force_cfg >= 0) {
         cfg = force_cfg;
     } else if (K % 8) {
-        cfg = 4;
+        cfg = CFG_W4_128x128_KMASK;
     } else if (M <= 32) {
-        cfg = 3;
+        cfg = CFG_W4_32x256;
     } else if (M <= 128) {
-        cfg = 2;
+        cfg = CFG_W4_128x128;
     } else if (M <= 256) {
-        cfg = 1;
+        // Decode batches: the whole of M in one 256-row tile, 128-wide in N so
+        // there are twice as many tiles as with 256, and split-K for the rest.
+        cfg = CFG_W4_256x128;
     } else {
+        // The 256x256 ping-pong tile when it fills at least half the machine on
+        // its own; smaller tiles otherwise.
         const int64_t big = cdiv(M, 256) * cdiv(N, 256);
-        cfg = big >= 128 ? 0 : 2;
+        cfg = big >= kNumCUs / 2 ? CFG_PP_256x256 : CFG_W4_128x128;
     }
     if ((K % 8) && !kConfigs[cfg].kmask)
-        cfg = 4;
+        cfg = CFG_W4_128x128_KMASK;
     const Config &c = kConfigs[cfg];
     p.cfg = cfg;
     p.tiles_m = (int)cdiv(M, c.bm);
     p.tiles_n = (int)cdiv(N, c.bn);
     p.k_tiles = (int)cdiv(K, c.bk);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-    const int64_t tile_bytes = (int64_t)c.bm * c.bn * 4;
 
     int splits = 1;
-    if (force_splits > 0) {
+    if (!c.splitk) {
+        splits = 1;
+    } else if (force_splits > 0) {
         splits = force_splits;
     } else if (tiles < kNumCUs && p.k_tiles >= 16) {
         // Fill the compute units, keeping at least 8 k-slabs per split.
@@ -128,9 +172,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         if (splits < 1)
             splits = 1;
     }
-    if (splits > 1 && tiles > kMaxCounters)
-        splits = 1;
-    while (splits > 1 && tiles * splits * tile_bytes > ws_bytes)
+    while (splits > 1 && (int64_t)splits * M * N * 4 > ws_bytes)
         --splits;
     if (p.k_tiles == 0)
         splits = 1;
@@ -144,7 +186,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     if (p.group_m < 1)
         p.group_m = 1;
     p.grid = tiles * splits;
-    p.ws_bytes = splits > 1 ? tiles * splits * tile_bytes : 0;
+    p.ws_bytes = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
     return p;
 }
 
@@ -153,7 +195,6 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
 struct gemm_handle_s {
     int device;
     float *partials;
-    unsigned *counters;
     int64_t ws_bytes;
     int force_cfg;
     int force_splits;
@@ -224,7 +265,7 @@ gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
     out->block_m = c.bm;
     out->block_n = c.bn;
     out->block_k = c.bk;
-    out->waves = c.wm * c.wn;
+    out->waves = c.waves;
     out->stages = c.stages;
     out->splits = p.splits;
     out->tiles = (int64_t)p.tiles_m * p.tiles_n;
@@ -269,19 +310,6 @@ gemm_status_t gemm_create(gemm_handle_t *out)
         delete h;
         return GEMM_ERR_ALLOC;
     }
-    if (hipMalloc(&h->counters, sizeof(unsigned) * kMaxCounters) != hipSuccess) {
-        (void)hipGetLastError();
-        (void)hipFree(h->partials);
-        delete h;
-        return GEMM_ERR_ALLOC;
-    }
-    if (hipMemset(h->counters, 0, sizeof(unsigned) * kMaxCounters) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
-        (void)hipFree(h->partials);
-        (void)hipFree(h->counters);
-        delete h;
-        return GEMM_ERR_HIP;
-    }
     *out = h;
     return GEMM_OK;
 }
@@ -292,8 +320,6 @@ gemm_status_t gemm_destroy(gemm_handle_t h)
         return GEMM_OK;
     gemm_status_t st = GEMM_OK;
     if (hipFree(h->partials) != hipSuccess)
-        st = GEMM_ERR_HIP;
-    if (hipFree(h->counters) != hipSuccess)
         st = GEMM_ERR_HIP;
     delete h;
     return st;
@@ -317,7 +343,7 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, i
         return GEMM_ERR_INVALID_ARG;
 
     const Plan p = make_plan(M, N, K, h->ws_bytes, h->force_cfg, h->force_splits);
-    if (p.splits > 1 && (p.ws_bytes > h->ws_bytes || (int64_t)p.tiles_m * p.tiles_n > kMaxCounters))
+    if (p.splits > 1 && p.ws_bytes > h->ws_bytes)
         return GEMM_ERR_UNSUPPORTED;
     if (p.grid <= 0 || p.grid >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
@@ -342,12 +368,13 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, i
     const uintptr_t vec_bytes = out_dtype == GEMM_FP32 ? 16 : 8;
     a.vec_store = (ldc % 4 == 0) && ((uintptr_t)C % vec_bytes == 0);
     a.partials = h->partials;
-    a.counters = h->counters;
     if (h->log)
         fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld\n",
                 (long long)M, (long long)N, (long long)K, c.name, p.tiles_m, p.tiles_n, p.splits,
                 p.kt_per_split, (long long)p.grid);
-    const hipError_t e = c.fn[in_dtype][out_dtype](a, (unsigned)p.grid, stream);
+    hipError_t e = c.fn[in_dtype][out_dtype](a, (unsigned)p.grid, stream);
+    if (e == hipSuccess && p.splits > 1)
+        e = launch_splitk_sum(a, out_dtype, stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 

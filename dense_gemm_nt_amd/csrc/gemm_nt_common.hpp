@@ -1,0 +1,213 @@
+// gemm_nt_common.hpp -- pieces shared by the gfx950 NT GEMM kernels: vector
+// types, the kernel argument block, buffer-resource and direct-to-LDS load
+// helpers, hand-placed waits and barriers, the MFMA wrapper, the LDS row
+// swizzle, the XCD-aware tile order and the epilogue store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gnt {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+enum : int { IN_BF16 = 0, IN_FP16 = 1 };
+enum : int { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2 };
+
+struct KernelArgs {
+    const uint16_t *A;
+    const uint16_t *B;
+    void *C;
+    int M, N, K;
+    int lda, ldb, ldc;     // elements
+    int tiles_m, tiles_n;
+    int k_tiles;           // ceil(K / BK)
+    int splits;            // K splits per tile (1 = none)
+    int kt_per_split;      // k-slabs per split
+    int group_m;           // tile rows per group of the tile order
+    int vec_store;         // 1 when 4 consecutive C elements may be stored as one vector
+    float *partials;       // split-K partials, dense [splits][M][N] FP32
+};
+
+// Byte offset added to a load that must return zeros: beyond every buffer's
+// num_records, so the buffer unit returns 0 without touching memory.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    // word 3: the gfx9 raw-buffer format (32-bit data, no swizzle, no stride).
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// One wave-wide 16-byte-per-lane load written straight into LDS at
+// lds_addr + 16 * lane.  Issued through asm so the compiler does not treat every
+// later LDS read as dependent on it; completion is tracked with vmcnt by hand.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                           uint32_t lds_addr)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr));
+}
+
+// One wave-wide 4-byte-per-lane load into LDS at lds_addr + 4 * lane.  Used to
+// pull cache lines into L2 ahead of their real load (the LDS bytes are dropped).
+__device__ __forceinline__ void touch_lds4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                           uint32_t lds_addr)
+{
+    asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int IN>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (IN == IN_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Swizzle key of LDS row r for a row of CH 16-byte chunks.  Depends only on
+// r mod 16, so every 32-row MFMA operand block sees the same pattern.
+template <int CH>
+__device__ __forceinline__ int row_key(int r)
+{
+    if constexpr (CH == 8)
+        return (r & 7) ^ ((r >> 3) & 1);
+    else
+        return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// Block id -> (tile row, tile column, K split).  See the header comment.
+__device__ __forceinline__ void map_block(int bid, int G, int tiles_m, int tiles_n, int group_m,
+                                          int &tm, int &tn, int &split)
+{
+    const int x = bid & 7, slot = bid >> 3;
+    const int q = G >> 3, r = G & 7;
+    const int v = x * q + (x < r ? x : r) + slot;
+    const int tiles = tiles_m * tiles_n;
+    split = v / tiles;
+    const int t = v - split * tiles;
+    const int per_group = group_m * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * group_m;
+    const int gsz = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int w = t - g * per_group;
+    tm = first_m + w % gsz;
+    tn = w / gsz;
+}
+
+template <int OUT>
+__device__ __forceinline__ void store4(void *C, int64_t idx, f32x4 v, bool vec, int valid)
+{
+    if constexpr (OUT == OUT_FP32) {
+        float *c = static_cast<float *>(C) + idx;
+        if (vec && valid >= 4) {
+            *reinterpret_cast<f32x4 *>(c) = v;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < valid)
+                    c[i] = v[i];
+        }
+    } else {
+        uint16_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (OUT == OUT_BF16)
+                h[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[i]));
+            else
+                h[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[i]));
+        }
+        uint16_t *c = static_cast<uint16_t *>(C) + idx;
+        if (vec && valid >= 4) {
+            u32x2 w;
+            w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            w[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            *reinterpret_cast<u32x2 *>(c) = w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < valid)
+                    c[i] = h[i];
+        }
+    }
+}
+
+// Zero the elements of an 8-value operand chunk from index `nvalid` on.
+__device__ __forceinline__ u32x4 mask_chunk(u32x4 x, int nvalid)
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t m = (2 * d < nvalid ? 0x0000FFFFu : 0u) | (2 * d + 1 < nvalid ? 0xFFFF0000u : 0u);
+        x[d] &= m;
+    }
+    return x;
+}
+
+// Epilogue of one lane's 4-element group C[m][n .. n+3] (n < N).  Without a
+// K split the FP32 sum is converted and stored into C; with one, the split's
+// FP32 partial goes to its slice of the workspace (dense [split][M][N]) and the
+// reduction kernel below finishes the job.
+template <int OUT>
+__device__ __forceinline__ void store_result(const KernelArgs &p, int split, int m, int n, f32x4 x)
+{
+    const int valid = p.N - n;
+    if (p.splits > 1) {
+        float *ws = p.partials + (int64_t)split * p.M * p.N;
+        store4<OUT_FP32>(ws, (int64_t)m * p.N + n, x, (p.N & 3) == 0, valid);
+    } else {
+        store4<OUT>(p.C, (int64_t)m * p.ldc + n, x, p.vec_store != 0, valid);
+    }
+}
+
+// Split-K reduction ("A Blackwell GEMM by Hand in CuTe DSL", section 9: each
+// CTA reduces a K slice, a second pass combines them).  One thread per group of
+// four consecutive outputs of a row adds the partials in split order 0, 1, ...
+// (a fixed order, so results are reproducible), converts, and stores.
+template <int OUT>
+__global__ __launch_bounds__(256) void splitk_sum(KernelArgs p)
+{
+    const int nvec = (p.N + 3) >> 2;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)p.M * nvec)
+        return;
+    const int m = (int)(t / nvec);
+    const int n = (int)(t - (int64_t)m * nvec) * 4;
+    const int valid = p.N - n;
+    const int64_t plane = (int64_t)p.M * p.N;
+    const float *src = p.partials + (int64_t)m * p.N + n;
+    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    if ((p.N & 3) == 0) {
+        for (int s = 0; s < p.splits; ++s)
+            sum += *reinterpret_cast<const f32x4 *>(src + s * plane);
+    } else {
+        for (int s = 0; s < p.splits; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < valid)
+                    sum[i] += src[s * plane + i];
+    }
+    store4<OUT>(p.C, (int64_t)m * p.ldc + n, sum, p.vec_store != 0, valid);
+}
+
+}  // namespace gnt

@@ -1,0 +1,106 @@
+"""Summarise rocprofv3 CSV output into the short text kept under profiles/.
+
+    python -m dense_gemm_nt_amd.profile_summary --stats DIR/run_kernel_stats.csv
+    python -m dense_gemm_nt_amd.profile_summary --counters DIR/fetch_counter_collection.csv \
+        [--copy-mb 512] [--skip 2]
+
+Counter mode averages each counter over the GEMM dispatches (after `--skip`
+warm-up launches) and, for FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scales the
+GEMM reading by the bytes a plain copy of --copy-mb MiB must move divided by what
+the same counter read for that copy.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+from collections import OrderedDict, defaultdict
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    return name if len(name) < 110 else name[:107] + "..."
+
+
+def stats(path):
+    out = []
+    for r in _rows(path):
+        out.append((r.get("Name") or r.get("KernelName") or "?", int(r.get("Calls", 0)),
+                    float(r.get("AverageNs", 0)), float(r.get("MinNs", 0)), float(r.get("MaxNs", 0)),
+                    float(r.get("Percentage", 0))))
+    return out
+
+
+def counters(path, skip):
+    per = defaultdict(lambda: defaultdict(list))   # kernel -> counter -> values in dispatch order
+    order = OrderedDict()
+    for r in _rows(path):
+        name = r.get("Kernel_Name") or r.get("Kernel-Name") or "?"
+        cn = r.get("Counter_Name") or r.get("Counter-Name")
+        cv = float(r.get("Counter_Value") or r.get("Counter-Value") or 0)
+        did = int(r.get("Dispatch_Id") or r.get("Dispatch-Id") or 0)
+        per[name][cn].append((did, cv))
+        order[name] = True
+    res = {}
+    for name in order:
+        res[name] = {}
+        for cn, vals in per[name].items():
+            vals.sort()
+            v = [x for _, x in vals]
+            if "gemm_nt_kernel" in name and len(v) > skip:
+                v = v[skip:]
+            res[name][cn] = (sum(v) / len(v), len(v))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--stats")
+    ap.add_argument("--counters")
+    ap.add_argument("--copy-mb", type=int, default=512)
+    ap.add_argument("--skip", type=int, default=2)
+    ap.add_argument("--json", action="store_true")
+    args = ap.parse_args()
+    if args.stats:
+        print("| kernel | calls | avg us | min us | max us | % time |")
+        print("|---|---|---|---|---|---|")
+        for n, c, a, lo, hi, pct in stats(args.stats):
+            print("| %s | %d | %.2f | %.2f | %.2f | %.1f |" % (_short(n), c, a / 1e3, lo / 1e3, hi / 1e3, pct))
+    if args.counters:
+        res = counters(args.counters, args.skip)
+        copy_bytes = args.copy_mb << 20
+        scale = {}
+        for name, cs in res.items():
+            if "copy" in name.lower() or "elementwise" in name.lower():
+                for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                    if cn in cs and cs[cn][0] > 0:
+                        scale[cn] = copy_bytes / (cs[cn][0] * 1024.0)
+        summary = {}
+        for name, cs in res.items():
+            for cn, (avg, n) in sorted(cs.items()):
+                line = {"avg": avg, "dispatches": n}
+                if cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                    line["bytes_raw"] = avg * 1024.0
+                    if cn in scale:
+                        line["calibration"] = scale[cn]
+                        line["bytes_calibrated"] = avg * 1024.0 * scale[cn]
+                summary.setdefault(_short(name), {})[cn] = line
+        if args.json:
+            print(json.dumps(summary, indent=1))
+        else:
+            for name, cs in summary.items():
+                print("kernel: %s" % name)
+                for cn, line in cs.items():
+                    extra = ""
+                    if "bytes_calibrated" in line:
+                        extra = "  -> %.1f MB (x%.3f from the copy calibration)" % (
+                            line["bytes_calibrated"] / 1e6, line["calibration"])
+                    print("  %-28s avg %.6g over %d dispatches%s" % (cn, line["avg"], line["dispatches"], extra))
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,7 @@
  * same device returns the same bits.
  *
  * Ownership: A, B and C are device pointers owned by the caller.  The handle
- * owns its workspace (split-K partial tiles and per-tile counters).
+ * owns its workspace (FP32 split-K partial sums).
  *
  * Streams: gemm_run only enqueues work on `stream` (0 = the null stream) and
  * never synchronises.  One handle must not be used by two calls that may run
@@ -55,8 +55,8 @@ typedef enum {
     GEMM_ERR_HIP = 5          /* a HIP runtime call or a launch failed */
 } gemm_status_t;
 
-/* Create a handle on the current device: allocates the split-K workspace and
- * zeroes its per-tile counters (synchronously).  *out is set to NULL on error. */
+/* Create a handle on the current device: allocates the split-K workspace
+ * (128 MiB by default; GEMM_WORKSPACE_MB overrides).  *out is NULL on error. */
 gemm_status_t gemm_create(gemm_handle_t *out);
 
 /* C = A . B^T (see the top of this file).
@@ -88,7 +88,7 @@ typedef struct {
     int splits;                    /* K splits per output tile (1 = none) */
     int64_t tiles;                 /* output tiles */
     int64_t workgroups;            /* grid size */
-    int64_t workspace_bytes;       /* split-K partials used */
+    int64_t workspace_bytes;       /* split-K partials used (splits * M * N * 4) */
     char name[48];                 /* kernel configuration name */
 } gemm_plan_t;
 
