@@ -14,7 +14,6 @@ the decode-regime shape M = 256, N = 28672, K = 8192 (A ~ N(0,1), B ~ N(0, 0.02^
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -25,16 +24,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2500.0     # MI355X dense BF16/FP16 MFMA, published
 HBM_TBS = 8.0            # MI355X HBM3E, published
-KERNEL_SOURCES = [os.path.join(ROOT, "dense_gemm_nt_amd", "csrc", f)
-                  for f in ("gemm_nt_kernel.hpp", "gemm_nt.hip")]
-
-
 def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from dense_gemm_nt_amd.profile_summary import kernel_hash as kh
+    return kh()
 
 
 def traffic_for(workload_key: str):
@@ -74,6 +66,14 @@ def time_gemm(g, shapes, steps, warmup, sets, in_dt, out_dt, dist):
                   code[in_dt], code[out_dt], sp)
 
     with torch.cuda.stream(stream):
+        # settle: clocks, TLBs and caches reach steady state before the counted
+        # warm-up steps (at least 0.3 s of back-to-back launches)
+        settle, t_settle = 0, time.perf_counter()
+        while time.perf_counter() - t_settle < 0.3:
+            for _ in range(10):
+                launch(settle)
+                settle += 1
+            torch.cuda.synchronize()
         for i in range(warmup):
             launch(i)
         torch.cuda.synchronize()
@@ -91,7 +91,7 @@ def time_gemm(g, shapes, steps, warmup, sets, in_dt, out_dt, dist):
     # the output of the last step, for a parity spot check
     last = (steps - 1) % sets
     h.close()
-    return wall_ms, event_ms, bufs, last
+    return wall_ms, event_ms, bufs, last, settle
 
 
 def spot_check(bufs, idx, shapes, in_dt, out_dt, dist):
@@ -139,7 +139,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the parity spot check")
     ap.add_argument("--quick", action="store_true", help="primary workload only")
@@ -159,8 +159,8 @@ def main():
 
     # primary: 4096^3 bf16 -> bf16, six rotating input sets (6 x 96 MB > 256 MB cache)
     shapes = (4096, 4096, 4096)
-    wall_ms, event_ms, bufs, last = time_gemm(g, shapes, args.steps, args.warmup, 6,
-                                              "bf16", "bf16", "uniform")
+    wall_ms, event_ms, bufs, last, settle = time_gemm(g, shapes, args.steps, args.warmup, 6,
+                                                      "bf16", "bf16", "uniform")
     worst = None if args.no_check else spot_check(bufs, last, shapes, "bf16", "bf16", "uniform")
     del bufs
     torch.cuda.empty_cache()
@@ -186,6 +186,7 @@ def main():
                    "M": M, "N": N, "K": K, "plan": plan["name"],
                    "pct_mfma_peak": round(100 * value / PEAK_TFLOPS, 2),
                    "cache": "cold: 6 rotating input sets (576 MB)",
+                   "settle_launches": settle,
                    "parity_worst_err_over_bound": worst},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
@@ -196,8 +197,8 @@ def main():
     if not args.quick:
         # decode-regime shape from the same metric: HBM-bound on this machine
         d = (256, 28672, 8192)
-        w2, e2, bufs, last = time_gemm(g, d, max(20, args.steps // 2), args.warmup, 2,
-                                       "bf16", "bf16", "llm")
+        w2, e2, bufs, last, _ = time_gemm(g, d, max(20, args.steps // 2), args.warmup, 2,
+                                          "bf16", "bf16", "llm")
         worst2 = None if args.no_check else spot_check(bufs, last, d, "bf16", "bf16", "llm")
         del bufs
         torch.cuda.empty_cache()

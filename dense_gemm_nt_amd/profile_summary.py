@@ -3,6 +3,8 @@
     python -m dense_gemm_nt_amd.profile_summary --stats DIR/run_kernel_stats.csv
     python -m dense_gemm_nt_amd.profile_summary --counters DIR/fetch_counter_collection.csv \
         [--copy-mb 512] [--skip 2]
+    python -m dense_gemm_nt_amd.profile_summary --traffic FETCH.csv WRITE.csv \
+        --key "4096^3 bf16->bf16" --update profiles/hbm_traffic.json
 
 Counter mode averages each counter over the GEMM dispatches (after `--skip`
 warm-up launches) and, for FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scales the
@@ -57,6 +59,38 @@ def counters(path, skip):
     return res
 
 
+def kernel_hash():
+    """Same hash bench.py compares against: the kernel sources as they are now."""
+    import hashlib
+    import os
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp", "gemm_nt_pingpong.hpp", "gemm_nt.hip"):
+        with open(os.path.join(root, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_csv, write_csv, copy_mb, skip):
+    """Calibrated HBM-side bytes per GEMM dispatch: (read, write, kernel name)."""
+    out = {}
+    for cn, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        res = counters(path, skip)
+        scale = None
+        for name, cs in res.items():
+            if ("copy" in name.lower()) and cn in cs and cs[cn][0] > 0:
+                scale = (copy_mb << 20) / (cs[cn][0] * 1024.0)
+        if scale is None:
+            raise SystemExit("no copy kernel found in %s for calibration" % path)
+        gemm = [(n, cs[cn][0]) for n, cs in res.items() if "gemm_nt" in n and cn in cs]
+        if not gemm:
+            raise SystemExit("no GEMM kernel in %s" % path)
+        # the dominant GEMM kernel (largest counter value) of the run
+        name, kib = max(gemm, key=lambda t: t[1])
+        out[cn] = (kib * 1024.0 * scale, scale, name)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stats")
@@ -64,7 +98,28 @@ def main():
     ap.add_argument("--copy-mb", type=int, default=512)
     ap.add_argument("--skip", type=int, default=2)
     ap.add_argument("--json", action="store_true")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--key", help="workload key for --traffic")
+    ap.add_argument("--update", help="JSON file to add the --traffic result to")
     args = ap.parse_args()
+    if args.traffic:
+        t = traffic(args.traffic[0], args.traffic[1], args.copy_mb, args.skip)
+        entry = {"bytes_per_launch": t["FETCH_SIZE"][0] + t["WRITE_SIZE"][0],
+                 "read_bytes": t["FETCH_SIZE"][0], "write_bytes": t["WRITE_SIZE"][0],
+                 "fetch_calibration": t["FETCH_SIZE"][1], "write_calibration": t["WRITE_SIZE"][1],
+                 "kernel": t["FETCH_SIZE"][2], "kernel_hash": kernel_hash()}
+        print(json.dumps({args.key: entry}, indent=1))
+        if args.update:
+            import os
+            d = {}
+            if os.path.exists(args.update):
+                with open(args.update) as f:
+                    d = json.load(f)
+            d[args.key] = entry
+            with open(args.update, "w") as f:
+                json.dump(d, f, indent=1, sort_keys=True)
+                f.write("\n")
+        return
     if args.stats:
         print("| kernel | calls | avg us | min us | max us | % time |")
         print("|---|---|---|---|---|---|")
