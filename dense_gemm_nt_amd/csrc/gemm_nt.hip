@@ -19,6 +19,7 @@
 #include "gemm_nt.h"
 #include "gemm_nt_kernel.hpp"
 #include "gemm_nt_pingpong.hpp"
+#include "gemm_nt_pingpong_split.hpp"
 
 namespace {
 
@@ -42,6 +43,13 @@ template <int IN, int OUT, int BK, int S, int PF>
 hipError_t launch_pingpong(const KernelArgs &a, unsigned grid, hipStream_t s)
 {
     hipLaunchKernelGGL((gnt::gemm_nt_pingpong<IN, OUT, BK, S, PF>), dim3(grid), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int IN, int OUT>
+hipError_t launch_pingpong_split(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gnt::gemm_nt_pingpong_split<IN, OUT>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
@@ -94,6 +102,9 @@ const Config kConfigs[] = {
     {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 1, 1, GNT_FNS(128, 128, 64, 2, 2, 4, true)},
     {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 0, 1, GNT_PP(64, 2, 0)},
     {"256x256x32_w8_pingpong_s5", 256, 256, 32, 8, 5, 0, 1, GNT_PP(32, 5, 0)},
+    {"256x256x64_w8_pingpong_split", 256, 256, 64, 8, 3, 0, 1,
+     {{launch_pingpong_split<0, 0>, launch_pingpong_split<0, 1>, launch_pingpong_split<0, 2>},
+      {launch_pingpong_split<1, 0>, launch_pingpong_split<1, 1>, launch_pingpong_split<1, 2>}}},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
@@ -367,6 +378,8 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, i
     a.group_m = p.group_m;
     const uintptr_t vec_bytes = out_dtype == GEMM_FP32 ? 16 : 8;
     a.vec_store = (ldc % 4 == 0) && ((uintptr_t)C % vec_bytes == 0);
+    const int64_t out_size = out_dtype == GEMM_FP32 ? 4 : 2;
+    a.rows16 = ((ldc * out_size) % 16 == 0) && ((uintptr_t)C % 16 == 0);
     a.partials = h->partials;
     if (h->log)
         fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld\n",

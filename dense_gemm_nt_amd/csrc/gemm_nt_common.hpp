@@ -31,6 +31,7 @@ struct KernelArgs {
     int kt_per_split;      // k-slabs per split
     int group_m;           // tile rows per group of the tile order
     int vec_store;         // 1 when 4 consecutive C elements may be stored as one vector
+    int rows16;            // 1 when every row of C starts 16-byte aligned
     float *partials;       // split-K partials, dense [splits][M][N] FP32
 };
 
@@ -177,6 +178,77 @@ __device__ __forceinline__ void store_result(const KernelArgs &p, int split, int
         store4<OUT_FP32>(ws, (int64_t)m * p.N + n, x, (p.N & 3) == 0, valid);
     } else {
         store4<OUT>(p.C, (int64_t)m * p.ldc + n, x, p.vec_store != 0, valid);
+    }
+}
+
+// Epilogue through LDS for one wave's 64 x 128 block of C (full tile only).
+// Staging C through shared memory and storing it with wide row-contiguous
+// writes is what "Optimizing GEMMs using tcgen05 - Part 1" measures as its last
+// phase (scattered stores replaced by one bulk store per block).  Here the
+// accumulator layout gives each lane four consecutive columns of one row, so
+// direct stores put only 16 bytes of a row per pair of lanes in each
+// instruction; staged through the wave's own 16 KB of LDS, every store
+// instruction writes whole 256- or 512-byte row segments.  The 16-byte chunk c
+// of staged row r sits at chunk c ^ (r mod 16) to keep the column-wise writes
+// off a single bank group.  Only the calling wave touches `stage`.
+// acc is [FN = 4][FM = 2] blocks of 32 x 32; the block's first element is
+// C[m0][n0] with m0, n0 relative to `dst`, which holds rows of `ld` elements.
+template <typename T>
+__device__ __forceinline__ void store_block_staged(const f32x16 (&acc)[4][2], uint8_t *stage, T *dst,
+                                                   int64_t ld, int lane)
+{
+    constexpr int ES = sizeof(T);
+    constexpr int ROWB = 128 * ES;           // staged row bytes (256 or 512)
+    constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+    constexpr int ROWS = 16384 / ROWB;       // rows per pass (64 or 32)
+    constexpr int PASSES = 64 / ROWS;
+    const int h = lane >> 5, r0 = lane & 31;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+        // write this pass's rows: fm blocks [pass * ROWS / 32, +ROWS / 32)
+#pragma unroll
+        for (int fmp = 0; fmp < ROWS / 32; ++fmp) {
+            const int fm = pass * (ROWS / 32) + fmp;
+            const int r = fmp * 32 + r0;   // row within this pass
+#pragma unroll
+            for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = fn * 32 + 8 * q + 4 * h;
+                    const int byte = col * ES;
+                    const int c = (byte >> 4) ^ (r & 15);
+                    uint8_t *a = stage + r * ROWB + c * 16 + (byte & 15);
+                    if constexpr (ES == 4) {
+                        f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                   acc[fn][fm][4 * q + 3]};
+                        *reinterpret_cast<f32x4 *>(a) = v;
+                    } else {
+                        uint16_t e[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (__is_same(T, __bf16))
+                                e[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[fn][fm][4 * q + i]));
+                            else
+                                e[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[fn][fm][4 * q + i]));
+                        }
+                        u32x2 w = {(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+                        *reinterpret_cast<u32x2 *>(a) = w;
+                    }
+                }
+        }
+        wait_lgkmcnt0();
+        // read back row-contiguous 16-byte chunks and store them
+        constexpr int LPR = CPR;             // lanes per row in one read
+        constexpr int RPR = 64 / LPR;        // rows per read instruction
+#pragma unroll
+        for (int j = 0; j < ROWS / RPR; ++j) {
+            const int r = j * RPR + lane / LPR;
+            const int c = lane % LPR;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * ROWB + ((c ^ (r & 15)) * 16));
+            T *g = dst + (int64_t)(pass * ROWS + r) * ld + c * (16 / ES);
+            *reinterpret_cast<u32x4 *>(g) = v;
+        }
+        wait_lgkmcnt0();
     }
 }
 

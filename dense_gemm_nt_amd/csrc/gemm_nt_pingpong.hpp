@@ -231,7 +231,26 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pingpong(KernelArgs p)
         }
     }
 
-    // Epilogue: lane holds C[m][n .. n+3] for each 4-register group.
+    // Epilogue.  Whole tiles go through LDS (the ring is free: the last LDS read
+    // of the main loop happened before its last barrier) and leave as
+    // row-contiguous 16-byte stores; edge tiles store straight from registers.
+    const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+    uint8_t *stage = smem + wave * 16384;
+    if (full && p.splits > 1 && (p.N & 3) == 0) {
+        float *ws = p.partials + (int64_t)split * p.M * p.N;
+        store_block_staged<float>(acc, stage, ws + (int64_t)(m0 + wm0) * p.N + (n0 + wn0), p.N, lane);
+        return;
+    }
+    if (full && p.splits == 1 && p.rows16) {
+        if constexpr (OUT == OUT_BF16)
+            store_block_staged<__bf16>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+        else if constexpr (OUT == OUT_FP16)
+            store_block_staged<_Float16>(acc, stage, static_cast<_Float16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+        else
+            store_block_staged<float>(acc, stage, static_cast<float *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+        return;
+    }
+    // lane holds C[m][n .. n+3] for each 4-register group
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int m = m0 + wm0 + fm * 32 + (lane & 31);

@@ -65,7 +65,8 @@ def kernel_hash():
     import os
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp", "gemm_nt_pingpong.hpp", "gemm_nt.hip"):
+    for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp", "gemm_nt_pingpong.hpp",
+              "gemm_nt_pingpong_split.hpp", "gemm_nt.hip"):
         with open(os.path.join(root, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -18,7 +18,8 @@ from tests.gpu_util import compare_full, compare_sampled, new_handle, run_gpu, s
 pytestmark = pytest.mark.gpu
 
 CONFIGS = ["256x256x64_w4_s2", "256x128x64_w4_s3", "128x128x64_w4_s4", "32x256x64_w4_s4",
-           "128x128x64_w4_s4_kmask", "256x256x64_w8_pingpong"]
+           "128x128x64_w4_s4_kmask", "256x256x64_w8_pingpong",
+           "256x256x64_w8_pingpong_split"]
 
 
 @pytest.fixture(scope="module")
