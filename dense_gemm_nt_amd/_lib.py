@@ -27,6 +27,7 @@ class GemmError(RuntimeError):
 class GemmPlan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("block_k", ctypes.c_int),
                 ("waves", ctypes.c_int), ("stages", ctypes.c_int), ("splits", ctypes.c_int),
+                ("lds_bytes", ctypes.c_int),
                 ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("name", ctypes.c_char * 48)]
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "gemm_nt.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp",
-                                           "gemm_nt_pingpong.hpp", "gemm_nt_pingpong_split.hpp")] + \
+                                           "gemm_nt_pingpong.hpp", "gemm_nt_pp2.hpp")] + \
     [os.path.join(ROOT, "include", "gemm_nt.h")]
 LIB = os.path.join(PKG, "libgemm_nt.so")
 ARCH = "gfx950"

@@ -19,7 +19,7 @@
 #include "gemm_nt.h"
 #include "gemm_nt_kernel.hpp"
 #include "gemm_nt_pingpong.hpp"
-#include "gemm_nt_pingpong_split.hpp"
+#include "gemm_nt_pp2.hpp"
 
 namespace {
 
@@ -47,11 +47,17 @@ hipError_t launch_pingpong(const KernelArgs &a, unsigned grid, hipStream_t s)
 }
 
 template <int IN, int OUT>
-hipError_t launch_pingpong_split(const KernelArgs &a, unsigned grid, hipStream_t s)
+hipError_t launch_pp2(const KernelArgs &a, unsigned grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gnt::gemm_nt_pingpong_split<IN, OUT>), dim3(grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((gnt::gemm_nt_pp2<IN, OUT>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
 }
+
+#define GNT_PP2                                                                                  \
+    {                                                                                            \
+        {launch_pp2<0, 0>, launch_pp2<0, 1>, launch_pp2<0, 2>},                                  \
+        {launch_pp2<1, 0>, launch_pp2<1, 1>, launch_pp2<1, 2>},                                  \
+    }
 
 #define GNT_PP(BK, S, PF)                                                                        \
     {                                                                                            \
@@ -77,6 +83,7 @@ hipError_t launch_splitk_sum(const KernelArgs &a, int out_dtype, hipStream_t s)
 struct Config {
     const char *name;
     int bm, bn, bk, waves, stages;
+    int lds;        // LDS bytes per workgroup
     int kmask;      // zeroes operand columns past K in registers (any K)
     int splitk;     // supports splits > 1
     launch_fn fn[2][3];   // [in dtype][out dtype]
@@ -95,16 +102,13 @@ struct Config {
 // Configurations with kmask = 1 zero the operand columns past K in registers and
 // are the only ones planned when K is not a multiple of 8.
 const Config kConfigs[] = {
-    {"256x256x64_w4_s2", 256, 256, 64, 4, 2, 0, 1, GNT_FNS(256, 256, 64, 2, 2, 2, false)},
-    {"256x128x64_w4_s3", 256, 128, 64, 4, 3, 0, 1, GNT_FNS(256, 128, 64, 2, 2, 3, false)},
-    {"128x128x64_w4_s4", 128, 128, 64, 4, 4, 0, 1, GNT_FNS(128, 128, 64, 2, 2, 4, false)},
-    {"32x256x64_w4_s4", 32, 256, 64, 4, 4, 0, 1, GNT_FNS(32, 256, 64, 1, 4, 4, false)},
-    {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 1, 1, GNT_FNS(128, 128, 64, 2, 2, 4, true)},
-    {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 0, 1, GNT_PP(64, 2, 0)},
-    {"256x256x32_w8_pingpong_s5", 256, 256, 32, 8, 5, 0, 1, GNT_PP(32, 5, 0)},
-    {"256x256x64_w8_pingpong_split", 256, 256, 64, 8, 3, 0, 1,
-     {{launch_pingpong_split<0, 0>, launch_pingpong_split<0, 1>, launch_pingpong_split<0, 2>},
-      {launch_pingpong_split<1, 0>, launch_pingpong_split<1, 1>, launch_pingpong_split<1, 2>}}},
+    {"256x256x64_w4_s2", 256, 256, 64, 4, 2, 131072, 0, 1, GNT_FNS(256, 256, 64, 2, 2, 2, false)},
+    {"256x128x64_w4_s3", 256, 128, 64, 4, 3, 147456, 0, 1, GNT_FNS(256, 128, 64, 2, 2, 3, false)},
+    {"128x128x64_w4_s4", 128, 128, 64, 4, 4, 131072, 0, 1, GNT_FNS(128, 128, 64, 2, 2, 4, false)},
+    {"32x256x64_w4_s4", 32, 256, 64, 4, 4, 147456, 0, 1, GNT_FNS(32, 256, 64, 1, 4, 4, false)},
+    {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 131072, 1, 1, GNT_FNS(128, 128, 64, 2, 2, 4, true)},
+    {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 131072, 0, 1, GNT_PP(64, 2, 0)},
+    {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, GNT_PP2},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
@@ -114,6 +118,7 @@ enum {
     CFG_W4_32x256 = 3,
     CFG_W4_128x128_KMASK = 4,
     CFG_PP_256x256 = 5,
+    CFG_PP2_256x256 = 6,
 };
 
 struct Plan {
@@ -152,14 +157,15 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     } else if (M <= 128) {
         cfg = CFG_W4_128x128;
     } else if (M <= 256) {
-        // Decode batches: the whole of M in one 256-row tile, 128-wide in N so
-        // there are twice as many tiles as with 256, and split-K for the rest.
-        cfg = CFG_W4_256x128;
+        // Decode batches: the whole of M in one 256-row tile of the ping-pong
+        // kernel (A stays in L2, every compute unit streams its own 256-row
+        // panel of B), and split-K below to bring the grid up to the machine.
+        cfg = CFG_PP2_256x256;
     } else {
         // The 256x256 ping-pong tile when it fills at least half the machine on
         // its own; smaller tiles otherwise.
         const int64_t big = cdiv(M, 256) * cdiv(N, 256);
-        cfg = big >= kNumCUs / 2 ? CFG_PP_256x256 : CFG_W4_128x128;
+        cfg = big >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_W4_128x128;
     }
     if ((K % 8) && !kConfigs[cfg].kmask)
         cfg = CFG_W4_128x128_KMASK;
@@ -278,6 +284,7 @@ gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
     out->block_k = c.bk;
     out->waves = c.waves;
     out->stages = c.stages;
+    out->lds_bytes = c.lds;
     out->splits = p.splits;
     out->tiles = (int64_t)p.tiles_m * p.tiles_n;
     out->workgroups = (M == 0 || N == 0) ? 0 : p.grid;

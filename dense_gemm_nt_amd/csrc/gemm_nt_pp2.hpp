@@ -1,0 +1,280 @@
+// gemm_nt_pp2.hpp -- eight-wave 256x256x64 ping-pong tile in which both wave
+// groups issue global loads, over an LDS ring of 16 KB units (gfx950).
+//
+// The phase structure is the one of gemm_nt_pingpong.hpp: two groups of four
+// waves (one wave of each group per SIMD) alternate between a memory phase
+// (LDS -> register fragment reads, plus direct-to-LDS global loads) and a
+// compute phase (the 32 MFMAs of one 64-deep k-slab), and a workgroup barrier
+// ends every phase.  What changes is who loads.  Issuing the 64 wave-wide
+// 1 KB loads of a slab takes longer than one compute phase when a single group
+// issues all of them: the vector memory unit accepts a wave-wide 16-byte-per-
+// lane load every ~25 cycles, so the loading waves stall on issue, not on
+// latency.  Here each group issues half a slab in its own memory phase, while
+// the other group keeps the matrix cores busy ("A Blackwell GEMM by Hand in
+// CuTe DSL", section 3: the producer's copies overlap the consumer's MMAs;
+// section 7: enough stages in flight for the load latency).
+//
+// Work split.  Group 0 owns tile rows 0..127 and group 1 rows 128..255, so
+// the A half of group g (A_g, 128 rows x 64 k = 16 KB) is read by that group
+// only, and B (256 rows, two 16 KB halves) by both.  The ring holds nine
+// 16 KB units: B in two slots of two units, A_0 in two units and A_1 in three.
+//
+//   phase 2i   : group 0 issues B(i+1), reads A_0(i) and B(i);
+//                group 1 computes slab i-1
+//   phase 2i+1 : group 1 issues A_0(i+2) and A_1(i+2), reads A_1(i) and B(i);
+//                group 0 computes slab i, then waits for B(i+1)
+//
+// Slot reuse: B(i+1) takes the slot of B(i-1), last read in phase 2i-1;
+// A_0(i+2) the unit of A_0(i), last read in phase 2i; A_1(i+2) the unit of
+// A_1(i-1), last read in phase 2i-1.  Group 1 waits, at the end of phase
+// 2i+1, until A(i+1) has landed (only A(i+2) may still be in flight); A(i+1)
+// is first read in phase 2i+2.  Each group waits only for its own loads
+// (vmcnt counts per wave), and the barrier that ends the phase publishes them.
+//
+// Output: wave w (group g = w / 4, q = w % 4) owns rows [128 g + 64 (q / 2), +64)
+// and columns [128 (q % 2), +128): 2 x 4 blocks of 32 x 32 with FP32
+// accumulators.  Requires K % 8 == 0.
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_nt_common.hpp"
+
+#ifndef GNT_PP2_EVENT
+#define GNT_PP2_EVENT(i, e)   // instrumentation hook (phase events); empty in the library
+#endif
+
+namespace gnt {
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
+{
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int PITCH = BK * 2;            // 128-byte LDS rows
+    constexpr int CH = BK / 8;               // 8 chunks per row
+    constexpr int UNIT = 128 * PITCH;        // 16 KB: 128 rows of one 64-deep slab
+    constexpr int U_B = 0;                   // B slot s: units 2s (rows 0..127), 2s+1
+    constexpr int U_A0 = 4;                  // A_0 slot s: unit 4 + s, s < 2
+    constexpr int U_A1 = 6;                  // A_1 slot s: unit 6 + s, s < 3
+    constexpr int UNITS = 9;
+    constexpr int FM = 2, FN = 4, KSTEPS = BK / 16;
+    static_assert(UNITS * UNIT <= 160 * 1024, "LDS budget");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[UNITS * UNIT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = wave >> 2;
+    const int q = wave & 3;
+    const int wm0 = group * 128 + (q >> 1) * 64;   // wave's first row within the tile
+    const int wn0 = (q & 1) * 128;                 // and first column
+
+    int tm, tn, split;
+    map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kt0 = split * p.kt_per_split;
+    const int nk = min(p.k_tiles, kt0 + p.kt_per_split) - kt0;
+
+    const int rows_a = min(BM, p.M - m0);
+    const int rows_b = min(BN, p.N - n0);
+    const __amdgpu_buffer_rsrc_t rsA =
+        make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)rows_a * (uint32_t)p.lda * 2u);
+    const __amdgpu_buffer_rsrc_t rsB =
+        make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)rows_b * (uint32_t)p.ldb * 2u);
+
+    // Load slots: within a 128-row unit, load j (0..3) of wave q covers rows
+    // 32 j + 8 q .. +8 (one 1 KB wave-wide load, 8 rows x 128 bytes).  The
+    // swizzle key depends on the row mod 16 only, so this lane's row offset and
+    // swizzled chunk are the same for every j and every unit.
+    const int lrow0 = q * 8 + lane / CH;
+    const int lc = (lane % CH) ^ row_key<CH>(lrow0);
+    const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+    const uint32_t voffA = (uint32_t)lrow0 * lda2 + (uint32_t)lc * 16u;
+    const uint32_t voffB = (uint32_t)lrow0 * ldb2 + (uint32_t)lc * 16u;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // Load number j (0..3) of the 128-row unit starting at tile row `row0` of
+    // A (IS_A) or B at local slab i into LDS unit u.
+    auto load_one = [&](auto is_a, int i, int row0, int u, int j) {
+        constexpr bool IS_A = decltype(is_a)::value;
+        const int kt = kt0 + i;
+        const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * 2);
+        const bool kin = lc * 8 < p.K - kt * BK;
+        const int row = row0 + 32 * j;
+        const int rows = IS_A ? rows_a : rows_b;
+        const uint32_t ld2 = IS_A ? lda2 : ldb2;
+        const uint32_t v = (kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange;
+        load_lds16(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2,
+                   lds0 + (uint32_t)(u * UNIT + (j * 4 + q) * 1024));
+    };
+    // The eight loads a wave issues in one memory phase, n = 0..7: group 0
+    // loads both halves of B(i) into B slot i % 2 (GRP = 0), group 1 both
+    // halves of A(i) (GRP = 1).
+    auto group_load = [&](auto grp, int i, int n) {
+        const int j = n & 3, half = n >> 2;
+        if constexpr (decltype(grp)::value == 0)
+            load_one(std::false_type{}, i, half * 128, U_B + 2 * (i & 1) + half, j);
+        else
+            load_one(std::true_type{}, i, half * 128, half == 0 ? U_A0 + (i & 1) : U_A1 + (i % 3), j);
+    };
+
+    int roff[KSTEPS];
+    {
+        const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            roff[ks] = r * PITCH + (((2 * ks + h) ^ row_key<CH>(r)) * 16);
+    }
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+
+    u32x4 af[KSTEPS][FM], bf[KSTEPS][FN];
+    // Fragment read number r (0..23) of local slab i: ks = r / 6, then the two
+    // A blocks and the four B blocks of that k16 step.
+    auto read_one = [&](auto grp, int i, int r) {
+        const int ks = r / 6, w = r % 6;
+        const int ua = decltype(grp)::value == 0 ? U_A0 + (i & 1) : U_A1 + (i % 3);
+        const uint8_t *sa = smem + ua * UNIT + (q >> 1) * 64 * PITCH;
+        const uint8_t *sb = smem + (U_B + 2 * (i & 1) + (q & 1)) * UNIT;
+        if (w < FM)
+            af[ks][w] = *reinterpret_cast<const u32x4 *>(sa + w * 32 * PITCH + roff[ks]);
+        else
+            bf[ks][w - FM] = *reinterpret_cast<const u32x4 *>(sb + (w - FM) * 32 * PITCH + roff[ks]);
+    };
+    // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
+    // fragment reads of slab i.  Loads first: their issue is what the vector
+    // memory unit paces, and the reads overlap it.
+    auto memory_phase = [&](auto grp, int i, bool has_load, int li) {
+        if (has_load)
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                group_load(grp, li, n);
+#pragma unroll
+        for (int r = 0; r < 24; ++r)
+            read_one(grp, i, r);
+    };
+    auto compute_slab = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fn][fm] = mfma32x32x16<IN>(bf[ks][fn], af[ks][fm], acc[fn][fm]);
+    };
+    auto phase_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        wg_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using G0 = std::integral_constant<int, 0>;
+    using G1 = std::integral_constant<int, 1>;
+
+    if (nk > 0) {
+        // Prologue: B(0) by group 0; A(0), A(1) by group 1.  Slab 0 lands before
+        // phase 0; A(1) by the end of phase 1 (the steady-state wait).
+        if (group == 0) {
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                group_load(G0{}, 0, n);
+            wait_vmcnt<0>();
+        } else {
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                group_load(G1{}, 0, n);
+            if (nk > 1) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                    group_load(G1{}, 1, n);
+                wait_vmcnt<8>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+        phase_end();
+        if (group == 0) {
+            for (int i = 0; i < nk; ++i) {
+                GNT_PP2_EVENT(i, 0);
+                memory_phase(G0{}, i, i + 1 < nk, i + 1);        // B(i+1)
+                wait_lgkmcnt0();
+                GNT_PP2_EVENT(i, 1);
+                phase_end();                               // end of phase 2i
+                GNT_PP2_EVENT(i, 2);
+                compute_slab();
+                __builtin_amdgcn_sched_barrier(0);
+                GNT_PP2_EVENT(i, 3);
+                wait_vmcnt<0>();                           // B(i+1) landed
+                GNT_PP2_EVENT(i, 4);
+                phase_end();                               // end of phase 2i+1
+            }
+        } else {
+            for (int i = 0; i < nk; ++i) {
+                GNT_PP2_EVENT(i, 0);
+                if (i > 0)
+                    compute_slab();                        // slab i-1
+                __builtin_amdgcn_sched_barrier(0);
+                GNT_PP2_EVENT(i, 1);
+                phase_end();                               // end of phase 2i
+                GNT_PP2_EVENT(i, 2);
+                memory_phase(G1{}, i, i + 2 < nk, i + 2);        // A(i+2)
+                wait_lgkmcnt0();
+                GNT_PP2_EVENT(i, 3);
+                if (i + 2 < nk)                            // A(i+1) landed
+                    wait_vmcnt<8>();
+                else
+                    wait_vmcnt<0>();
+                GNT_PP2_EVENT(i, 4);
+                phase_end();                               // end of phase 2i+1
+            }
+            compute_slab();                                // slab nk-1
+        }
+    }
+
+    // Epilogue (the ring is free: the last fragment read and the last load
+    // completed before the loop's last barrier).  Each wave stages its own
+    // 64 x 128 block in its own 16 KB of LDS.
+    const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+    uint8_t *stage = smem + wave * 16384;
+    if (full && p.splits > 1 && (p.N & 3) == 0) {
+        float *ws = p.partials + (int64_t)split * p.M * p.N;
+        store_block_staged<float>(acc, stage, ws + (int64_t)(m0 + wm0) * p.N + (n0 + wn0), p.N, lane);
+        return;
+    }
+    if (full && p.splits == 1 && p.rows16) {
+        if constexpr (OUT == OUT_BF16)
+            store_block_staged<__bf16>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+        else if constexpr (OUT == OUT_FP16)
+            store_block_staged<_Float16>(acc, stage, static_cast<_Float16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+        else
+            store_block_staged<float>(acc, stage, static_cast<float *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+        return;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + wm0 + fm * 32 + (lane & 31);
+        if (m >= p.M)
+            continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn0 + fn * 32 + 8 * g + 4 * (lane >> 5);
+                if (n >= p.N)
+                    continue;
+                f32x4 x = {acc[fn][fm][4 * g], acc[fn][fm][4 * g + 1], acc[fn][fm][4 * g + 2],
+                           acc[fn][fm][4 * g + 3]};
+                store_result<OUT>(p, split, m, n, x);
+            }
+        }
+    }
+}
+
+}  // namespace gnt

@@ -1,6 +1,7 @@
 """Summarise rocprofv3 CSV output into the short text kept under profiles/.
 
     python -m dense_gemm_nt_amd.profile_summary --stats DIR/run_kernel_stats.csv
+    python -m dense_gemm_nt_amd.profile_summary --trace DIR/run_kernel_trace.csv
     python -m dense_gemm_nt_amd.profile_summary --counters DIR/fetch_counter_collection.csv \
         [--copy-mb 512] [--skip 2]
     python -m dense_gemm_nt_amd.profile_summary --traffic FETCH.csv WRITE.csv \
@@ -37,6 +38,21 @@ def stats(path):
     return out
 
 
+def trace_groups(path):
+    """Per-dispatch kernel trace grouped by (kernel, workgroups): one workload each
+    when one kernel serves several grid shapes.  Durations in ns."""
+    groups = OrderedDict()
+    for r in _rows(path):
+        name = r.get("Kernel_Name") or "?"
+        wg = int(r.get("Workgroup_Size_X") or 1) * int(r.get("Workgroup_Size_Y") or 1) * \
+            int(r.get("Workgroup_Size_Z") or 1)
+        grid = int(r.get("Grid_Size_X") or 0) * int(r.get("Grid_Size_Y") or 1) * \
+            int(r.get("Grid_Size_Z") or 1)
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        groups.setdefault((name, grid // max(wg, 1)), []).append(d)
+    return groups
+
+
 def counters(path, skip):
     per = defaultdict(lambda: defaultdict(list))   # kernel -> counter -> values in dispatch order
     order = OrderedDict()
@@ -53,7 +69,7 @@ def counters(path, skip):
         for cn, vals in per[name].items():
             vals.sort()
             v = [x for _, x in vals]
-            if "gemm_nt_kernel" in name and len(v) > skip:
+            if "gnt::" in name and len(v) > skip:
                 v = v[skip:]
             res[name][cn] = (sum(v) / len(v), len(v))
     return res
@@ -66,7 +82,7 @@ def kernel_hash():
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
     for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp", "gemm_nt_pingpong.hpp",
-              "gemm_nt_pingpong_split.hpp", "gemm_nt.hip"):
+              "gemm_nt_pp2.hpp", "gemm_nt.hip"):
         with open(os.path.join(root, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -95,6 +111,7 @@ def traffic(fetch_csv, write_csv, copy_mb, skip):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stats")
+    ap.add_argument("--trace")
     ap.add_argument("--counters")
     ap.add_argument("--copy-mb", type=int, default=512)
     ap.add_argument("--skip", type=int, default=2)
@@ -126,6 +143,12 @@ def main():
         print("|---|---|---|---|---|---|")
         for n, c, a, lo, hi, pct in stats(args.stats):
             print("| %s | %d | %.2f | %.2f | %.2f | %.1f |" % (_short(n), c, a / 1e3, lo / 1e3, hi / 1e3, pct))
+    if args.trace:
+        print("| kernel | workgroups | calls | avg us | min us | max us |")
+        print("|---|---|---|---|---|---|")
+        for (n, wgs), ds in trace_groups(args.trace).items():
+            print("| %s | %d | %d | %.2f | %.2f | %.2f |" % (_short(n), wgs, len(ds), sum(ds) / len(ds) / 1e3,
+                                                          min(ds) / 1e3, max(ds) / 1e3))
     if args.counters:
         res = counters(args.counters, args.skip)
         copy_bytes = args.copy_mb << 20

@@ -84,8 +84,9 @@ gemm_status_t gemm_validate(const void *A, const void *B, void *C, int64_t M, in
 typedef struct {
     int block_m, block_n, block_k; /* output tile and K depth of one LDS stage */
     int waves;                     /* wavefronts per workgroup */
-    int stages;                    /* LDS ring depth */
+    int stages;                    /* LDS ring slots (the 256x256 ping-pong kernel: 16 KB units) */
     int splits;                    /* K splits per output tile (1 = none) */
+    int lds_bytes;                 /* LDS the kernel allocates per workgroup */
     int64_t tiles;                 /* output tiles */
     int64_t workgroups;            /* grid size */
     int64_t workspace_bytes;       /* split-K partials used (splits * M * N * 4) */

