@@ -182,10 +182,13 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     } else if (force_splits > 0) {
         splits = force_splits;
     } else if (tiles < kNumCUs && p.k_tiles >= 16) {
-        // Fill the compute units, keeping at least 8 k-slabs per split.
+        // Fill the compute units, keeping at least 8 k-slabs per split (20 for
+        // the 256x256 tile, whose 256 KB FP32 partial per split costs as much
+        // as streaming about 4 slabs of B).
+        const int min_slabs = cfg == CFG_PP2_256x256 ? 20 : 8;
         splits = (int)(kNumCUs / tiles);
-        if (splits > p.k_tiles / 8)
-            splits = p.k_tiles / 8;
+        if (splits > p.k_tiles / min_slabs)
+            splits = p.k_tiles / min_slabs;
         if (splits < 1)
             splits = 1;
     }

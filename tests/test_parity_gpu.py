@@ -96,6 +96,20 @@ def test_small_integers_bitwise(config, splits):
     hh.close()
 
 
+@pytest.mark.parametrize("config", ["256x256x64_w8_pp2", "256x256x64_w8_pingpong"])
+@pytest.mark.parametrize("K", [8, 64, 128, 192, 200])
+def test_short_k_bitwise(config, K):
+    # one to four k-slabs: the prologue and drain paths of the multi-slab rings
+    M, N = 300, 280
+    say("case short-K int3 bitwise config=%s M=%d N=%d K=%d" % (config, M, N, K))
+    hh = new_handle(config)
+    A, B = make_operands(M, N, K, "bf16", "int3", seed=K, lda=ld8(K + 8), ldb=ld8(K))
+    C = run_gpu(hh, A, B, K, "bf16", "fp32")
+    Cr, _ = oracle.gemm_nt(A, B, K=K, in_dtype="bf16")
+    assert np.array_equal(C, Cr)
+    hh.close()
+
+
 # ------------------------------------------------------------ closed forms
 
 @pytest.mark.parametrize("K,outd", [(257, "bf16"), (259, "bf16"), (5000, "bf16"), (5000, "fp16"),
