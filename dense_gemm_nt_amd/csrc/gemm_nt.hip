@@ -309,8 +309,13 @@ gemm_status_t gemm_create(gemm_handle_t *out)
     int64_t mb = kDefaultWorkspaceMB;
     if (const char *e = getenv("GEMM_WORKSPACE_MB"))
         mb = atoll(e) > 0 ? atoll(e) : mb;
-    if (const char *e = getenv("GEMM_CONFIG"))
+    if (const char *e = getenv("GEMM_CONFIG")) {
         h->force_cfg = find_config(e);
+        if (h->force_cfg < 0) {   // a named kernel that does not exist is an error, not a fallback
+            delete h;
+            return GEMM_ERR_INVALID_ARG;
+        }
+    }
     if (const char *e = getenv("GEMM_SPLITS"))
         h->force_splits = atoi(e);
     if (const char *e = getenv("GEMM_LOG"))

@@ -56,7 +56,10 @@ typedef enum {
 } gemm_status_t;
 
 /* Create a handle on the current device: allocates the split-K workspace
- * (128 MiB by default; GEMM_WORKSPACE_MB overrides).  *out is NULL on error. */
+ * (128 MiB by default; GEMM_WORKSPACE_MB overrides).  *out is NULL on error.
+ * For measurement, GEMM_CONFIG=<name> forces one kernel configuration and
+ * GEMM_SPLITS=<n> a K split on every call of this handle; a GEMM_CONFIG that
+ * names no configuration makes gemm_create return GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_create(gemm_handle_t *out);
 
 /* C = A . B^T (see the top of this file).

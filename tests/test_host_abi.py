@@ -83,6 +83,16 @@ def test_create_rejects_null_out(g):
     assert _lib.lib().gemm_create(None) == 1
 
 
+def test_create_rejects_unknown_forced_config_before_device_work(g, monkeypatch):
+    # a measurement override naming no kernel must fail, not fall back silently
+    import ctypes
+    from dense_gemm_nt_amd import _lib
+    monkeypatch.setenv("GEMM_CONFIG", "no_such_kernel")
+    h = ctypes.c_void_p(12345)
+    assert _lib.lib().gemm_create(ctypes.byref(h)) == 1
+    assert h.value is None
+
+
 LDS_BYTES = 160 * 1024
 
 
