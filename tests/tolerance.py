@@ -56,3 +56,35 @@ def check(C_gpu, C_ref, S, out_dtype, what=""):
             % (what, tuple(int(i) for i in idx), c[idx], r[idx], s[idx], err[idx], bound[idx],
                int((ratio > 1.0).sum())))
     return (float(err.max()) if err.size else 0.0), worst
+
+
+def check_epilogue(D_gpu, D_ref, aS, t, out_dtype, what=""):
+    """Acceptance of a fused-epilogue result D = act(alpha acc + beta C_old + bias).
+
+    aS = |alpha| S and t = |beta C_old| + |bias| (oracle.epilogue.scale_of).  The
+    sum's own bound 1e-3 S + 1e-5 is scaled by |alpha| and by 1.2 (the largest
+    slope of GELU is 1.13; ReLU's is 1); 2^-20 (|alpha| S + t) covers the FP32
+    multiply-adds after the sum and the activation's evaluation; the output
+    ulp covers the final rounding.
+    """
+    c = np.asarray(D_gpu, dtype=np.float64)
+    r = np.asarray(D_ref, dtype=np.float64)
+    if c.shape != r.shape:
+        raise AssertionError("%s: shape %r vs oracle %r" % (what, c.shape, r.shape))
+    if not np.all(np.isfinite(c)):
+        bad = np.argwhere(~np.isfinite(c))[:5]
+        raise AssertionError("%s: non-finite output at %s" % (what, bad.tolist()))
+    aS = np.asarray(aS, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    err = np.abs(c - r)
+    bound = 1.2 * (REL * aS + ABS) + 2.0 ** -20 * (aS + t) + \
+        ulp(np.maximum(np.abs(r), np.abs(c)), out_dtype)
+    ratio = err / bound
+    worst = float(ratio.max()) if ratio.size else 0.0
+    if worst > 1.0:
+        idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        raise AssertionError(
+            "%s: |D-D_ref| above bound at %s: gpu=%r ref=%r err=%r bound=%r (%d elements over)"
+            % (what, tuple(int(i) for i in idx), c[idx], r[idx], err[idx], bound[idx],
+               int((ratio > 1.0).sum())))
+    return (float(err.max()) if err.size else 0.0), worst
