@@ -9,11 +9,12 @@ LIB_PATH = os.path.join(PKG, "libgemm_nt.so")
 
 GEMM_BF16, GEMM_FP16, GEMM_FP32 = 0, 1, 2
 GEMM_OK = 0
+GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED, GEMM_ERR_MISALIGNED = 1, 2, 3
 STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_UNSUPPORTED",
           3: "GEMM_ERR_MISALIGNED", 4: "GEMM_ERR_ALLOC", 5: "GEMM_ERR_HIP"}
 
 # Every symbol include/gemm_nt.h declares.
-EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_validate", "gemm_plan",
+EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_destroy", "gemm_validate", "gemm_plan",
            "gemm_status_string")
 
 
@@ -37,6 +38,14 @@ class GemmPlan(ctypes.Structure):
         return d
 
 
+class GemmEpilogue(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("bias", ctypes.c_void_p),
+                ("bias_along", ctypes.c_int), ("activation", ctypes.c_int)]
+
+
+BIAS_ALONG = {"none": 0, "n": 1, "m": 2}
+ACTIVATION = {"none": 0, "relu": 1, "gelu": 2}
+
 _lib = None
 
 
@@ -56,6 +65,9 @@ def lib():
     L.gemm_destroy.restype = ci
     L.gemm_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci, vp]
     L.gemm_run.restype = ci
+    L.gemm_run_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci,
+                              ctypes.POINTER(GemmEpilogue), vp]
+    L.gemm_run_ex.restype = ci
     L.gemm_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci]
     L.gemm_validate.restype = ci
     L.gemm_plan.argtypes = [i64, i64, i64, ci, ci, ctypes.POINTER(GemmPlan)]
@@ -84,6 +96,22 @@ def gemm_destroy(h):
 def gemm_run(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, stream):
     """Raw entry point: A, B, C and stream are integer device addresses / a hipStream_t."""
     return lib().gemm_run(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, stream)
+
+
+def gemm_run_ex(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, epi, stream):
+    """Raw entry point with a fused epilogue (a GemmEpilogue or None)."""
+    return lib().gemm_run_ex(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype,
+                             ctypes.byref(epi) if epi is not None else None, stream)
+
+
+def epilogue(alpha=1.0, beta=0.0, bias=0, bias_along="none", activation="none"):
+    """A GemmEpilogue; `bias` is an integer device address (0 for none)."""
+    if bias_along not in BIAS_ALONG:
+        raise ValueError("bias_along must be one of %s" % sorted(BIAS_ALONG))
+    if activation not in ACTIVATION:
+        raise ValueError("activation must be one of %s" % sorted(ACTIVATION))
+    return GemmEpilogue(float(alpha), float(beta), bias or None, BIAS_ALONG[bias_along],
+                        ACTIVATION[activation])
 
 
 def gemm_validate(A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype):

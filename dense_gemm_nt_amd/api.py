@@ -37,11 +37,21 @@ class Gemm:
         st = _lib.gemm_run(self._h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, stream)
         _lib.check(st, "gemm_run(M=%d, N=%d, K=%d)" % (M, N, K))
 
-    def __call__(self, A, B, out=None, out_dtype=None, stream=None):
-        """C = A . B^T for CUDA tensors A [M, K] and B [N, K] (unit column stride)."""
+    def run_raw_ex(self, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, epi, stream):
+        st = _lib.gemm_run_ex(self._h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, epi,
+                              stream)
+        _lib.check(st, "gemm_run_ex(M=%d, N=%d, K=%d)" % (M, N, K))
+
+    def __call__(self, A, B, out=None, out_dtype=None, stream=None, alpha=1.0, beta=0.0,
+                 bias=None, bias_along="n", activation="none"):
+        """C = act(alpha * A . B^T + beta * C_old + bias) for CUDA tensors A [M, K] and
+        B [N, K] (unit column stride).  beta != 0 needs `out` holding C_old; `bias` is
+        a float32 CUDA tensor of N values (bias_along="n") or M values ("m")."""
         import torch
         if A.dim() != 2 or B.dim() != 2:
             raise ValueError("A and B must be 2-D")
+        if beta != 0.0 and out is None:
+            raise ValueError("beta != 0 reads the prior C: pass it as `out`")
         M, K = A.shape
         N, K2 = B.shape
         if K != K2:
@@ -60,8 +70,23 @@ class Gemm:
         ldc = out.stride(0) if M > 1 else max(N, out.stride(0))
         if stream is None:
             stream = torch.cuda.current_stream(A.device).cuda_stream
-        self.run_raw(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc,
-                     _code(A.dtype), _code(out.dtype), stream)
+        plain = alpha == 1.0 and beta == 0.0 and bias is None and activation == "none"
+        if plain:
+            self.run_raw(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc,
+                         _code(A.dtype), _code(out.dtype), stream)
+            return out
+        along = "none"
+        if bias is not None:
+            along = bias_along
+            want = N if along == "n" else M
+            if bias.dtype != torch.float32 or bias.dim() != 1 or bias.numel() != want \
+                    or bias.stride(0) != 1 or bias.device != A.device:
+                raise ValueError("bias must be a contiguous float32 vector of %d values on %s"
+                                 % (want, A.device))
+        epi = _lib.epilogue(alpha, beta, bias.data_ptr() if bias is not None else 0, along,
+                            activation)
+        self.run_raw_ex(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc,
+                        _code(A.dtype), _code(out.dtype), epi, stream)
         return out
 
 
@@ -78,8 +103,10 @@ def default_handle(device_index: int) -> Gemm:
         return h
 
 
-def gemm_nt(A, B, out=None, out_dtype=None):
-    """C = A . B^T on A's device with the per-device default handle (current stream)."""
+def gemm_nt(A, B, out=None, out_dtype=None, **epilogue):
+    """C = A . B^T on A's device with the per-device default handle (current stream);
+    keyword arguments alpha, beta, bias, bias_along, activation select the fused
+    epilogue (see Gemm.__call__)."""
     import torch
     with torch.cuda.device(A.device):
-        return default_handle(A.device.index)(A, B, out=out, out_dtype=out_dtype)
+        return default_handle(A.device.index)(A, B, out=out, out_dtype=out_dtype, **epilogue)

@@ -14,6 +14,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <cmath>
 #include <new>
 
 #include "gemm_nt.h"
@@ -355,11 +356,28 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, i
                        int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype,
                        hipStream_t stream)
 {
+    return gemm_run_ex(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, nullptr, stream);
+}
+
+gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C, int64_t M,
+                          int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int in_dtype,
+                          int out_dtype, const gemm_epilogue_t *epi, hipStream_t stream)
+{
     if (!h)
         return GEMM_ERR_INVALID_ARG;
     gemm_status_t st = gemm_validate(A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype);
     if (st != GEMM_OK)
         return st;
+    if (epi) {
+        if (epi->bias_along < GEMM_BIAS_NONE || epi->bias_along > GEMM_BIAS_M)
+            return GEMM_ERR_INVALID_ARG;
+        if (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)
+            return GEMM_ERR_INVALID_ARG;
+        if (epi->bias_along != GEMM_BIAS_NONE && (!epi->bias || (uintptr_t)epi->bias % 4))
+            return GEMM_ERR_INVALID_ARG;
+        if (!std::isfinite(epi->alpha) || !std::isfinite(epi->beta))
+            return GEMM_ERR_UNSUPPORTED;
+    }
     if (M == 0 || N == 0)
         return GEMM_OK;
     int dev = -1;
@@ -396,6 +414,17 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, i
     const int64_t out_size = out_dtype == GEMM_FP32 ? 4 : 2;
     a.rows16 = ((ldc * out_size) % 16 == 0) && ((uintptr_t)C % 16 == 0);
     a.partials = h->partials;
+    a.alpha = 1.0f;
+    if (epi) {
+        a.alpha = epi->alpha;
+        a.beta = epi->beta;
+        a.bias = epi->bias_along != GEMM_BIAS_NONE ? epi->bias : nullptr;
+        a.bias_along = epi->bias_along;
+        a.act = epi->activation;
+        a.bias_vec = ((uintptr_t)a.bias % 16) == 0;
+        a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && a.bias_along == GEMM_BIAS_NONE &&
+                  a.act == GEMM_ACT_NONE);
+    }
     if (h->log)
         fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld\n",
                 (long long)M, (long long)N, (long long)K, c.name, p.tiles_m, p.tiles_n, p.splits,

@@ -33,6 +33,13 @@ struct KernelArgs {
     int vec_store;         // 1 when 4 consecutive C elements may be stored as one vector
     int rows16;            // 1 when every row of C starts 16-byte aligned
     float *partials;       // split-K partials, dense [splits][M][N] FP32
+    // fused epilogue D = act(alpha * acc + beta * C_old + bias), applied when epi != 0
+    float alpha, beta;
+    const float *bias;     // FP32, N values (bias_along == 1) or M values (2)
+    int bias_along;        // 0 none, 1 along n (one per column), 2 along m (one per row)
+    int act;               // 0 none, 1 ReLU, 2 GELU (x * Phi(x), erf form)
+    int bias_vec;          // 1 when the bias pointer is 16-byte aligned
+    int epi;               // 1 when the epilogue is not the identity
 };
 
 // Byte offset added to a load that must return zeros: beyond every buffer's
@@ -165,6 +172,109 @@ __device__ __forceinline__ u32x4 mask_chunk(u32x4 x, int nvalid)
     return x;
 }
 
+// The prior contents of C[m][n .. n+3] (the first `valid` of them) as FP32.
+template <int OUT>
+__device__ __forceinline__ f32x4 load4(const void *C, int64_t idx, bool vec, int valid)
+{
+    f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (OUT == OUT_FP32) {
+        const float *c = static_cast<const float *>(C) + idx;
+        if (vec && valid >= 4) {
+            r = *reinterpret_cast<const f32x4 *>(c);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < valid)
+                    r[i] = c[i];
+        }
+    } else {
+        const uint16_t *c = static_cast<const uint16_t *>(C) + idx;
+        uint16_t h[4] = {0, 0, 0, 0};
+        if (vec && valid >= 4) {
+            const u32x2 w = *reinterpret_cast<const u32x2 *>(c);
+            h[0] = (uint16_t)w[0];
+            h[1] = (uint16_t)(w[0] >> 16);
+            h[2] = (uint16_t)w[1];
+            h[3] = (uint16_t)(w[1] >> 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < valid)
+                    h[i] = c[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (OUT == OUT_BF16)
+                r[i] = static_cast<float>(__builtin_bit_cast(__bf16, h[i]));
+            else
+                r[i] = static_cast<float>(__builtin_bit_cast(_Float16, h[i]));
+        }
+    }
+    return r;
+}
+
+// GELU in its exact form x * Phi(x) = x / 2 * (1 + erf(x / sqrt 2)), with erf
+// from Abramowitz and Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2),
+// t = 1 / (1 + p z) for z >= 0, odd in z, |error| <= 1.5e-7.  About a dozen
+// VALU operations against several dozen for the library erf; the formula's
+// error, below 2^-22 of |x| in the result, is inside the epilogue's bound.
+__device__ __forceinline__ float gelu_erf(float x)
+{
+    const float z = fabsf(x) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
+    float poly = 1.061405429f;
+    poly = poly * t - 1.453152027f;
+    poly = poly * t + 1.421413741f;
+    poly = poly * t - 0.284496736f;
+    poly = poly * t + 0.254829592f;
+    const float e = 1.0f - poly * t * __expf(-z * z);   // erf(|x| / sqrt 2)
+    return 0.5f * x * (1.0f + copysignf(e, x));
+}
+
+// Fused epilogue ("CUTLASS Deep Dive", the Tutorial 01/05 epilogues and the
+// EVT / "Bias + ReLU" passages: alpha times the accumulator plus beta times
+// the existing C, plus a bias, through an activation, in one pass as the tile
+// is written back) on the FP32 sums of C[m][n .. n+3], the first `valid` of
+// which are inside the output.  Every value is read and then written by the
+// same lane, so reading C_old here is race-free.
+template <int OUT>
+__device__ __forceinline__ f32x4 epilogue4(const KernelArgs &p, int m, int n, f32x4 x, int valid)
+{
+    const int64_t idx = (int64_t)m * p.ldc + n;
+    f32x4 old = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.beta != 0.0f)
+        old = load4<OUT>(p.C, idx, p.vec_store != 0, valid);
+    // n is a multiple of 4 at every call, so bias + n is 16-byte aligned with bias
+    f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.bias_along == 1) {
+        if (p.bias_vec && valid >= 4) {
+            b = *reinterpret_cast<const f32x4 *>(p.bias + n);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < valid)
+                    b[i] = p.bias[n + i];
+        }
+    } else if (p.bias_along == 2) {
+        const float bm = p.bias[m];
+        b = (f32x4){bm, bm, bm, bm};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = p.alpha * x[i];
+        if (p.beta != 0.0f)
+            v += p.beta * old[i];
+        v += b[i];
+        if (p.act == 1)
+            v = fmaxf(v, 0.0f);
+        else if (p.act == 2)
+            v = gelu_erf(v);
+        x[i] = v;
+    }
+    return x;
+}
+
 // Epilogue of one lane's 4-element group C[m][n .. n+3] (n < N).  Without a
 // K split the FP32 sum is converted and stored into C; with one, the split's
 // FP32 partial goes to its slice of the workspace (dense [split][M][N]) and the
@@ -177,6 +287,8 @@ __device__ __forceinline__ void store_result(const KernelArgs &p, int split, int
         float *ws = p.partials + (int64_t)split * p.M * p.N;
         store4<OUT_FP32>(ws, (int64_t)m * p.N + n, x, (p.N & 3) == 0, valid);
     } else {
+        if (p.epi)
+            x = epilogue4<OUT>(p, m, n, x, valid);
         store4<OUT>(p.C, (int64_t)m * p.ldc + n, x, p.vec_store != 0, valid);
     }
 }
@@ -252,6 +364,127 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&acc)[4][2], ui
     }
 }
 
+// Raw prior-C values of four consecutive outputs (aligned vector load) and
+// their FP32 values.
+template <int OUT>
+struct OldC {
+    typedef u32x2 raw;
+};
+template <>
+struct OldC<OUT_FP32> {
+    typedef f32x4 raw;
+};
+template <int OUT>
+__device__ __forceinline__ typename OldC<OUT>::raw load_old4(const void *C, int64_t idx)
+{
+    if constexpr (OUT == OUT_FP32)
+        return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(C) + idx);
+    else
+        return *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(C) + idx);
+}
+template <int OUT>
+__device__ __forceinline__ f32x4 old4_value(typename OldC<OUT>::raw w)
+{
+    if constexpr (OUT == OUT_FP32) {
+        return w;
+    } else {
+        f32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t h = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+            if constexpr (OUT == OUT_BF16)
+                r[i] = static_cast<float>(__builtin_bit_cast(__bf16, h));
+            else
+                r[i] = static_cast<float>(__builtin_bit_cast(_Float16, h));
+        }
+        return r;
+    }
+}
+
+// The staged whole-tile store with the fused epilogue: a wave's 64 x 128 block
+// goes through its 16 KB of LDS as FP32, 32 rows per pass, and the epilogue is
+// applied on the way out, where each lane holds four consecutive columns of
+// one row: the bias and prior-C loads are then row-contiguous vectors, and
+// the accumulators need no extra registers.  The lane's bias vector is the
+// same for every row; the prior C values of each step of rows are loaded one
+// step ahead (the first before the staging writes), so their round trips
+// overlap the LDS traffic and the arithmetic.  The first element of the
+// block is C[m0][n0].
+template <int OUT>
+__device__ __forceinline__ void store_block_staged_epi(const KernelArgs &p, const f32x16 (&acc)[4][2],
+                                                       uint8_t *stage, int m0, int n0, int lane)
+{
+    constexpr int ROWB = 512;                // 128 FP32 per staged row
+    typedef typename OldC<OUT>::raw raw_t;
+    const int h = lane >> 5, r0 = lane & 31;
+    const int c = lane & 31, n = n0 + 4 * c;  // read-back chunk of this lane
+    const bool has_old = p.beta != 0.0f;
+    f32x4 bn = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.bias_along == 1)
+        bn = p.bias_vec ? *reinterpret_cast<const f32x4 *>(p.bias + n)
+                        : (f32x4){p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
+    // step s = SP fm + t covers rows fm * 32 + 2 (J t + j) + lane / 32, j < J: 8-row
+    // steps for 16-bit outputs, 4-row steps for FP32 (whose prior values take
+    // twice the registers)
+    constexpr int J = OUT == OUT_FP32 ? 4 : 8, SP = 16 / J;
+    auto row_of = [&](int st, int j) { return (st / SP) * 32 + 2 * (J * (st % SP) + j) + (lane >> 5); };
+    raw_t cur[J], nxt[J];
+    if (has_old)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            cur[j] = load_old4<OUT>(p.C, (int64_t)(m0 + row_of(0, j)) * p.ldc + n);
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+        // write rows fm*32 .. +32 (chunk c of row r at c ^ (r mod 16))
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = fn * 32 + 8 * q + 4 * h;
+                const int cc = (col >> 2) ^ (r0 & 15);
+                f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                           acc[fn][fm][4 * q + 3]};
+                *reinterpret_cast<f32x4 *>(stage + r0 * ROWB + cc * 16) = v;
+            }
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            const int st = SP * fm + t;
+            if (has_old && st + 1 < 2 * SP)
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    nxt[j] = load_old4<OUT>(p.C, (int64_t)(m0 + row_of(st + 1, j)) * p.ldc + n);
+            f32x4 x[J];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int r = row_of(st, j) - fm * 32;
+                x[j] = *reinterpret_cast<const f32x4 *>(stage + r * ROWB + ((c ^ (r & 15)) * 16));
+            }
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int m = m0 + row_of(st, j);
+                const float bm = p.bias_along == 2 ? p.bias[m] : 0.0f;
+                const f32x4 old = has_old ? old4_value<OUT>(cur[j]) : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = p.alpha * x[j][e] + p.beta * old[e] + bn[e] + bm;
+                    if (p.act == 1)
+                        v = fmaxf(v, 0.0f);
+                    else if (p.act == 2)
+                        v = gelu_erf(v);
+                    y[e] = v;
+                }
+                store4<OUT>(p.C, (int64_t)m * p.ldc + n, y, true, 4);
+            }
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                cur[j] = nxt[j];
+        }
+        wait_lgkmcnt0();
+    }
+}
+
 // Split-K reduction ("A Blackwell GEMM by Hand in CuTe DSL", section 9: each
 // CTA reduces a K slice, a second pass combines them).  One thread per group of
 // four consecutive outputs of a row adds the partials in split order 0, 1, ...
@@ -279,6 +512,8 @@ __global__ __launch_bounds__(256) void splitk_sum(KernelArgs p)
                 if (i < valid)
                     sum[i] += src[s * plane + i];
     }
+    if (p.epi)
+        sum = epilogue4<OUT>(p, m, n, sum, valid);
     store4<OUT>(p.C, (int64_t)m * p.ldc + n, sum, p.vec_store != 0, valid);
 }
 

@@ -248,6 +248,10 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
         store_block_staged<float>(acc, stage, ws + (int64_t)(m0 + wm0) * p.N + (n0 + wn0), p.N, lane);
         return;
     }
+    if (full && p.splits == 1 && p.rows16 && p.epi) {
+        store_block_staged_epi<OUT>(p, acc, stage, m0 + wm0, n0 + wn0, lane);
+        return;
+    }
     if (full && p.splits == 1 && p.rows16) {
         if constexpr (OUT == OUT_BF16)
             store_block_staged<__bf16>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);

@@ -74,6 +74,38 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C,
                        int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                        int in_dtype, int out_dtype, hipStream_t stream);
 
+/* Fused epilogue ("CUTLASS Deep Dive: From CuTe Layouts to Blackwell tcgen05",
+ * the Tutorial 01/05 epilogues, "Epilogue Visitor Trees (EVT)" and "Classic
+ * Fused Epilogue: Bias + ReLU"): as each output tile is written back,
+ *     C[i,j] = act( alpha * sum_k A[i,k] B[j,k] + beta * C_old[i,j] + bias )
+ * computed in FP32 and rounded once to out_dtype (round to nearest even).
+ *   alpha, beta  FP32 scalars; beta != 0 reads the prior contents of C
+ *   bias         device pointer to FP32 values, 4-byte aligned, caller-owned:
+ *                N of them (bias_along GEMM_BIAS_N: one per output column, the
+ *                bias of a linear layer whose weights are the rows of B) or M
+ *                (GEMM_BIAS_M: one per output row); NULL when GEMM_BIAS_NONE
+ *   activation   GEMM_ACT_NONE, GEMM_ACT_RELU (max(0, x)) or GEMM_ACT_GELU
+ *                (x * Phi(x) = x / 2 * (1 + erf(x / sqrt(2))))  */
+typedef enum { GEMM_BIAS_NONE = 0, GEMM_BIAS_N = 1, GEMM_BIAS_M = 2 } gemm_bias_t;
+typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU = 2 } gemm_act_t;
+typedef struct {
+    float alpha;
+    float beta;
+    const float *bias;
+    int bias_along;  /* gemm_bias_t */
+    int activation;  /* gemm_act_t */
+} gemm_epilogue_t;
+
+/* gemm_run with a fused epilogue.  epi == NULL is the plain product
+ * (alpha = 1, beta = 0, no bias, no activation).  Errors as gemm_run, plus
+ * GEMM_ERR_INVALID_ARG for an unknown bias_along or activation, a missing or
+ * misaligned bias, and GEMM_ERR_UNSUPPORTED for a non-finite alpha or beta.
+ * With beta != 0, C must hold the prior output values. */
+gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C,
+                          int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                          int in_dtype, int out_dtype, const gemm_epilogue_t *epi,
+                          hipStream_t stream);
+
 /* Release the handle and its workspace.  NULL is a no-op.  The caller must make
  * sure no call enqueued with this handle is still running. */
 gemm_status_t gemm_destroy(gemm_handle_t h);
