@@ -74,6 +74,33 @@ def make_operands(M, N, K, dtype="bf16", dist="uniform", seed=0, lda=None, ldb=N
     return A.contiguous(), B.contiguous()
 
 
+def store(X, layout, ld=None):
+    """Lay the logical operand X [rows, K] out in memory: "k" keeps it row-major
+    ([rows][ld >= K]); "mn" stores its transpose ([K][ld >= rows]).  Padding
+    columns hold NaN."""
+    rows, K = X.shape
+    if layout == "k":
+        src, extent = X, K
+    elif layout == "mn":
+        src, extent = X.t(), rows
+    else:
+        raise ValueError("unknown layout %r" % (layout,))
+    ld = extent if ld is None else ld
+    if ld < extent:
+        raise ValueError("leading dimension below the stored row length")
+    out = torch.full((src.shape[0], ld), float("nan"), dtype=X.dtype)
+    out[:, :extent] = src
+    return out.contiguous()
+
+
+def make_stored(M, N, K, layout_a="k", layout_b="k", dtype="bf16", dist="uniform", seed=0,
+                lda=None, ldb=None):
+    """make_operands' values (same seed, same bits), each operand laid out by
+    store(): A as [M][lda] or [K][lda], B as [N][ldb] or [K][ldb]."""
+    A, B = make_operands(M, N, K, dtype, dist, seed)
+    return store(A, layout_a, lda), store(B, layout_b, ldb)
+
+
 def rotation_sets(M, N, K, dtype, dist, seed, count):
     """`count` independent operand pairs (seeds seed, seed+1, ...) for cold-cache timing."""
     return [make_operands(M, N, K, dtype, dist, seed + i) for i in range(count)]

@@ -177,6 +177,58 @@ def gemm_nt_points(A, B, ii, jj, K=None, in_dtype="bf16"):
     return C, S
 
 
+LAYOUTS = ("k", "mn")
+
+
+def logical_operand(X, layout, rows=None, K=None) -> np.ndarray:
+    """The [rows, K] operand (codes) that a stored array X holds.
+
+    Page "Steps for Writing a Speed-of-Light GEMM kernel: Part 1", the CuTe
+    introduction ("A tensor is storage plus a layout"): a layout maps the
+    logical coordinate to a storage offset, (m, k) -> m * ld + k for a
+    row-major (K-major) operand.  An MN-major operand stores the same matrix
+    with the roles of the two indices exchanged, (m, k) -> k * ld + m, i.e. X is
+    [K][>= rows] and the operand is its transpose.  Page "Optimizing GEMMs using
+    tcgen05 - Part 1" ("What I am measuring") multiplies a row-major A [M, K] by
+    a row-major B [K, N]: here that B is the N-major operand of A . B^T.
+    """
+    c = _codes(X)
+    if c.ndim != 2:
+        raise ValueError("operand must be 2-D")
+    if layout == "k":
+        rows = c.shape[0] if rows is None else rows
+        K = c.shape[1] if K is None else K
+        if c.shape[0] < rows or c.shape[1] < K:
+            raise ValueError("stored %r does not cover %d x %d" % (c.shape, rows, K))
+        return c[:rows, :K]
+    if layout == "mn":
+        rows = c.shape[1] if rows is None else rows
+        K = c.shape[0] if K is None else K
+        if c.shape[1] < rows or c.shape[0] < K:
+            raise ValueError("stored %r does not cover %d x %d (transposed)" % (c.shape, K, rows))
+        return np.ascontiguousarray(c[:K, :rows].T)
+    raise ValueError("unknown layout %r" % (layout,))
+
+
+def gemm(A, B, layout_a="k", layout_b="k", K=None, in_dtype="bf16", with_abs=True):
+    """C_ref, S of sum_k a(i,k) b(j,k) with each operand read through its layout
+    (logical_operand); (k, k) is gemm_nt."""
+    a = logical_operand(A, layout_a, K=K)
+    b = logical_operand(B, layout_b, K=K)
+    if a.shape[1] != b.shape[1]:
+        raise ValueError("inner dimensions differ: %d vs %d" % (a.shape[1], b.shape[1]))
+    return gemm_nt(a, b, in_dtype=in_dtype, with_abs=with_abs)
+
+
+def gemm_points(A, B, ii, jj, layout_a="k", layout_b="k", K=None, in_dtype="bf16"):
+    """C_ref[p], S[p] at (ii[p], jj[p]) of the product gemm() defines."""
+    a = logical_operand(A, layout_a, K=K)
+    b = logical_operand(B, layout_b, K=K)
+    if a.shape[1] != b.shape[1]:
+        raise ValueError("inner dimensions differ: %d vs %d" % (a.shape[1], b.shape[1]))
+    return gemm_nt_points(a, b, ii, jj, in_dtype=in_dtype)
+
+
 def decode(codes, in_dtype="bf16") -> np.ndarray:
     """Exact binary64 values of an array of 16-bit codes."""
     lib = _load()
