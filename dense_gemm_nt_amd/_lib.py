@@ -14,8 +14,8 @@ STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_UNSUPPORTED",
           3: "GEMM_ERR_MISALIGNED", 4: "GEMM_ERR_ALLOC", 5: "GEMM_ERR_HIP"}
 
 # Every symbol include/gemm_nt.h declares.
-EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_destroy", "gemm_validate", "gemm_plan",
-           "gemm_status_string")
+EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_run_layout", "gemm_destroy",
+           "gemm_validate", "gemm_plan", "gemm_status_string")
 
 
 class GemmError(RuntimeError):
@@ -44,6 +44,7 @@ class GemmEpilogue(ctypes.Structure):
 
 
 BIAS_ALONG = {"none": 0, "n": 1, "m": 2}
+GEMM_K_MAJOR, GEMM_MN_MAJOR = 0, 1
 ACTIVATION = {"none": 0, "relu": 1, "gelu": 2}
 
 _lib = None
@@ -68,6 +69,9 @@ def lib():
     L.gemm_run_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci,
                               ctypes.POINTER(GemmEpilogue), vp]
     L.gemm_run_ex.restype = ci
+    L.gemm_run_layout.argtypes = [vp, ci, ci, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci,
+                                  ctypes.POINTER(GemmEpilogue), vp]
+    L.gemm_run_layout.restype = ci
     L.gemm_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci]
     L.gemm_validate.restype = ci
     L.gemm_plan.argtypes = [i64, i64, i64, ci, ci, ctypes.POINTER(GemmPlan)]
@@ -102,6 +106,13 @@ def gemm_run_ex(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype, epi, st
     """Raw entry point with a fused epilogue (a GemmEpilogue or None)."""
     return lib().gemm_run_ex(h, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype,
                              ctypes.byref(epi) if epi is not None else None, stream)
+
+
+def gemm_run_layout(h, layout_a, layout_b, A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype,
+                    epi, stream):
+    """Raw entry point for any operand layouts (GEMM_K_MAJOR / GEMM_MN_MAJOR each)."""
+    return lib().gemm_run_layout(h, layout_a, layout_b, A, B, C, M, N, K, lda, ldb, ldc, in_dtype,
+                                 out_dtype, ctypes.byref(epi) if epi is not None else None, stream)
 
 
 def epilogue(alpha=1.0, beta=0.0, bias=0, bias_along="none", activation="none"):

@@ -16,6 +16,19 @@ def _code(dtype) -> int:
     return c
 
 
+def _operand(X, rows, K):
+    """(layout, leading dimension) of a [rows, K] operand view: K-major when its
+    K stride is 1, MN-major (a transposed view of a [K, rows] array) when its row
+    stride is 1."""
+    if K == 0 or rows == 0:
+        return _lib.GEMM_K_MAJOR, max(K, 1)
+    if X.stride(1) == 1 and (rows == 1 or X.stride(0) >= K):
+        return _lib.GEMM_K_MAJOR, X.stride(0) if rows > 1 else max(K, X.stride(0))
+    if X.stride(0) == 1 and (K == 1 or X.stride(1) >= rows):
+        return _lib.GEMM_MN_MAJOR, X.stride(1) if K > 1 else max(rows, X.stride(1))
+    raise ValueError("operand strides %s are neither K-major nor MN-major" % (tuple(X.stride()),))
+
+
 class Gemm:
     """A library handle (workspace owner) bound to the current device."""
 
@@ -42,11 +55,19 @@ class Gemm:
                               stream)
         _lib.check(st, "gemm_run_ex(M=%d, N=%d, K=%d)" % (M, N, K))
 
+    def run_raw_layout(self, layout_a, layout_b, A, B, C, M, N, K, lda, ldb, ldc, in_dtype,
+                       out_dtype, epi, stream):
+        st = _lib.gemm_run_layout(self._h, layout_a, layout_b, A, B, C, M, N, K, lda, ldb, ldc,
+                                  in_dtype, out_dtype, epi, stream)
+        _lib.check(st, "gemm_run_layout(%d, %d, M=%d, N=%d, K=%d)" % (layout_a, layout_b, M, N, K))
+
     def __call__(self, A, B, out=None, out_dtype=None, stream=None, alpha=1.0, beta=0.0,
                  bias=None, bias_along="n", activation="none"):
         """C = act(alpha * A . B^T + beta * C_old + bias) for CUDA tensors A [M, K] and
-        B [N, K] (unit column stride).  beta != 0 needs `out` holding C_old; `bias` is
-        a float32 CUDA tensor of N values (bias_along="n") or M values ("m")."""
+        B [N, K].  Each operand is K-major (unit stride along K) or MN-major (unit
+        stride along its rows: e.g. B = W.t() for a row-major W [K, N]).  beta != 0
+        needs `out` holding C_old; `bias` is a float32 CUDA tensor of N values
+        (bias_along="n") or M values ("m")."""
         import torch
         if A.dim() != 2 or B.dim() != 2:
             raise ValueError("A and B must be 2-D")
@@ -58,20 +79,19 @@ class Gemm:
             raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
         if A.dtype != B.dtype:
             raise TypeError("A and B must share a dtype")
-        if K > 0 and (A.stride(1) != 1 or B.stride(1) != 1):
-            raise ValueError("A and B need unit stride along K")
+        la, lda = _operand(A, M, K)
+        lb, ldb = _operand(B, N, K)
         if out is None:
             out_dtype = A.dtype if out_dtype is None else out_dtype
             out = torch.empty((M, N), dtype=out_dtype, device=A.device)
         if out.dim() != 2 or tuple(out.shape) != (M, N) or (N > 0 and out.stride(1) != 1):
             raise ValueError("out must be [M, N] with unit column stride")
-        lda = A.stride(0) if M > 1 else max(K, A.stride(0))
-        ldb = B.stride(0) if N > 1 else max(K, B.stride(0))
         ldc = out.stride(0) if M > 1 else max(N, out.stride(0))
         if stream is None:
             stream = torch.cuda.current_stream(A.device).cuda_stream
         plain = alpha == 1.0 and beta == 0.0 and bias is None and activation == "none"
-        if plain:
+        nt = la == _lib.GEMM_K_MAJOR and lb == _lib.GEMM_K_MAJOR
+        if plain and nt:
             self.run_raw(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc,
                          _code(A.dtype), _code(out.dtype), stream)
             return out
@@ -83,8 +103,12 @@ class Gemm:
                     or bias.stride(0) != 1 or bias.device != A.device:
                 raise ValueError("bias must be a contiguous float32 vector of %d values on %s"
                                  % (want, A.device))
-        epi = _lib.epilogue(alpha, beta, bias.data_ptr() if bias is not None else 0, along,
-                            activation)
+        epi = None if plain else _lib.epilogue(alpha, beta, bias.data_ptr() if bias is not None
+                                               else 0, along, activation)
+        if not nt:
+            self.run_raw_layout(la, lb, A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lda,
+                                ldb, ldc, _code(A.dtype), _code(out.dtype), epi, stream)
+            return out
         self.run_raw_ex(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc,
                         _code(A.dtype), _code(out.dtype), epi, stream)
         return out

@@ -1,17 +1,24 @@
 """Compile the HIP library (gfx950) in place: ``python -m dense_gemm_nt_amd.build``."""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, "gemm_nt.hip")]
+# the host side and one translation unit per group of kernel instantiations,
+# compiled in parallel and linked into one shared library
+SOURCES = [os.path.join(CSRC, f) for f in (
+    "gemm_nt.hip", "launch_tiles_a.hip", "launch_tiles_b.hip", "launch_pingpong.hip",
+    "launch_pp2.hip", "launch_pp2_km.hip", "launch_pp2_mk.hip", "launch_pp2_mm.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp",
-                                           "gemm_nt_pingpong.hpp", "gemm_nt_pp2.hpp")] + \
+                                           "gemm_nt_pingpong.hpp", "gemm_nt_pp2.hpp",
+                                           "gemm_nt_launch.hpp")] + \
     [os.path.join(ROOT, "include", "gemm_nt.h")]
 LIB = os.path.join(PKG, "libgemm_nt.so")
 ARCH = "gfx950"
@@ -24,24 +31,47 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str, extra=()) -> list:
-    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+def flags() -> list:
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
             # packed FP32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument", *extra, *SOURCES, "-o", out]
+            "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def command(out: str, extra=()) -> list:
+    """One hipcc line that compiles and links every source (used by tools that
+    want a single command, e.g. with extra -R remarks)."""
+    return [hipcc(), *flags(), "-shared", *extra, *SOURCES, "-o", out]
+
+
+def _run(cmd):
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(ln for ln in res.stdout.splitlines() if "packed-fp32-ops" not in ln)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    os.replace(tmp, LIB)
+        raise RuntimeError("hipcc failed: %s\n%s" % (" ".join(cmd), out))
+    return out
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    tmpdir = tempfile.mkdtemp(prefix="gemm_nt_build_")
+    try:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *flags(), "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(_run, cmds))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        link = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        _run(link)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

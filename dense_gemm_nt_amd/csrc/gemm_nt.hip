@@ -18,55 +18,20 @@
 #include <new>
 
 #include "gemm_nt.h"
-#include "gemm_nt_kernel.hpp"
-#include "gemm_nt_pingpong.hpp"
-#include "gemm_nt_pp2.hpp"
+#include "gemm_nt_launch.hpp"
 
 namespace {
 
 using gnt::KernelArgs;
+using gnt::launch_fn;
 
 constexpr int kNumCUs = 256;
 constexpr int64_t kMaxLeadingDim = (int64_t)1 << 22;   // keeps tile byte offsets below 2^31
 constexpr int64_t kDefaultWorkspaceMB = 128;
 
-typedef hipError_t (*launch_fn)(const KernelArgs &, unsigned grid, hipStream_t);
-
-template <int BM, int BN, int BK, int WM, int WN, int ST, int IN, int OUT, bool KMASK>
-hipError_t launch_cfg(const KernelArgs &a, unsigned grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((gnt::gemm_nt_kernel<BM, BN, BK, WM, WN, ST, IN, OUT, KMASK>), dim3(grid),
-                       dim3(WM * WN * 64), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int IN, int OUT, int BK, int S, int PF>
-hipError_t launch_pingpong(const KernelArgs &a, unsigned grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((gnt::gemm_nt_pingpong<IN, OUT, BK, S, PF>), dim3(grid), dim3(512), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int IN, int OUT>
-hipError_t launch_pp2(const KernelArgs &a, unsigned grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((gnt::gemm_nt_pp2<IN, OUT>), dim3(grid), dim3(512), 0, s, a);
-    return hipGetLastError();
-}
-
-#define GNT_PP2                                                                                  \
-    {                                                                                            \
-        {launch_pp2<0, 0>, launch_pp2<0, 1>, launch_pp2<0, 2>},                                  \
-        {launch_pp2<1, 0>, launch_pp2<1, 1>, launch_pp2<1, 2>},                                  \
-    }
-
-#define GNT_PP(BK, S, PF)                                                                        \
-    {                                                                                            \
-        {launch_pingpong<0, 0, BK, S, PF>, launch_pingpong<0, 1, BK, S, PF>,                     \
-         launch_pingpong<0, 2, BK, S, PF>},                                                      \
-        {launch_pingpong<1, 0, BK, S, PF>, launch_pingpong<1, 1, BK, S, PF>,                     \
-         launch_pingpong<1, 2, BK, S, PF>},                                                      \
-    }
+// The 256x256 ping-pong tile for the other operand layouts, indexed by
+// 2 * (A MN-major) + (B MN-major) - 1.
+launch_fn (*const kLayoutFns[3])[3] = {gnt::kPP2_km, gnt::kPP2_mk, gnt::kPP2_mm};
 
 hipError_t launch_splitk_sum(const KernelArgs &a, int out_dtype, hipStream_t s)
 {
@@ -87,29 +52,21 @@ struct Config {
     int lds;        // LDS bytes per workgroup
     int kmask;      // zeroes operand columns past K in registers (any K)
     int splitk;     // supports splits > 1
-    launch_fn fn[2][3];   // [in dtype][out dtype]
+    launch_fn (*fn)[3];   // [in dtype][out dtype]
 };
 
-#define GNT_FNS(BM, BN, BK, WM, WN, ST, KM)                                                      \
-    {                                                                                            \
-        {launch_cfg<BM, BN, BK, WM, WN, ST, 0, 0, KM>, launch_cfg<BM, BN, BK, WM, WN, ST, 0, 1, KM>, \
-         launch_cfg<BM, BN, BK, WM, WN, ST, 0, 2, KM>},                                          \
-        {launch_cfg<BM, BN, BK, WM, WN, ST, 1, 0, KM>, launch_cfg<BM, BN, BK, WM, WN, ST, 1, 1, KM>, \
-         launch_cfg<BM, BN, BK, WM, WN, ST, 1, 2, KM>},                                          \
-    }
-
-// The kernel family.  LDS per workgroup = stages * (BM + BN) * BK * 2 bytes, at
-// most 160 KB; each wave owns a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-// Configurations with kmask = 1 zero the operand columns past K in registers and
-// are the only ones planned when K is not a multiple of 8.
+// The kernel family.  The kernel-template tiles use stages * (BM + BN) * BK * 2
+// bytes of LDS (at most 160 KB) and give each wave a (BM/WM) x (BN/WN) block of
+// 32x32 MFMA tiles.  Configurations with kmask = 1 zero the operand columns past
+// K in registers and are the only ones planned when K is not a multiple of 8.
 const Config kConfigs[] = {
-    {"256x256x64_w4_s2", 256, 256, 64, 4, 2, 131072, 0, 1, GNT_FNS(256, 256, 64, 2, 2, 2, false)},
-    {"256x128x64_w4_s3", 256, 128, 64, 4, 3, 147456, 0, 1, GNT_FNS(256, 128, 64, 2, 2, 3, false)},
-    {"128x128x64_w4_s4", 128, 128, 64, 4, 4, 131072, 0, 1, GNT_FNS(128, 128, 64, 2, 2, 4, false)},
-    {"32x256x64_w4_s4", 32, 256, 64, 4, 4, 147456, 0, 1, GNT_FNS(32, 256, 64, 1, 4, 4, false)},
-    {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 131072, 1, 1, GNT_FNS(128, 128, 64, 2, 2, 4, true)},
-    {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 131072, 0, 1, GNT_PP(64, 2, 0)},
-    {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, GNT_PP2},
+    {"256x256x64_w4_s2", 256, 256, 64, 4, 2, 131072, 0, 1, gnt::kTile256x256_w4_s2},
+    {"256x128x64_w4_s3", 256, 128, 64, 4, 3, 147456, 0, 1, gnt::kTile256x128_w4_s3},
+    {"128x128x64_w4_s4", 128, 128, 64, 4, 4, 131072, 0, 1, gnt::kTile128x128_w4_s4},
+    {"32x256x64_w4_s4", 32, 256, 64, 4, 4, 147456, 0, 1, gnt::kTile32x256_w4_s4},
+    {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 131072, 1, 1, gnt::kTile128x128_w4_s4_kmask},
+    {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 131072, 0, 1, gnt::kPingpong256},
+    {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
@@ -237,8 +194,11 @@ const char *gemm_status_string(int s)
     }
 }
 
-gemm_status_t gemm_validate(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
-                            int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype)
+// The argument checks of every run; a_row / b_row are the extents a row of A /
+// B holds (K for a K-major operand, M or N for an MN-major one).
+static gemm_status_t validate(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                              int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t a_row,
+                              int64_t b_row, int in_dtype, int out_dtype)
 {
     if (in_dtype != GEMM_BF16 && in_dtype != GEMM_FP16)
         return GEMM_ERR_UNSUPPORTED;
@@ -246,7 +206,7 @@ gemm_status_t gemm_validate(const void *A, const void *B, void *C, int64_t M, in
         return GEMM_ERR_UNSUPPORTED;
     if (M < 0 || N < 0 || K < 0)
         return GEMM_ERR_INVALID_ARG;
-    if (lda < K || ldb < K || ldc < N || lda < 0 || ldb < 0)
+    if (lda < a_row || ldb < b_row || ldc < N || lda < 0 || ldb < 0)
         return GEMM_ERR_INVALID_ARG;
     if (M >= INT32_MAX || N >= INT32_MAX || K >= INT32_MAX || ldc >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
@@ -266,6 +226,12 @@ gemm_status_t gemm_validate(const void *A, const void *B, void *C, int64_t M, in
     if ((uintptr_t)A % 16 || (uintptr_t)B % 16 || lda % 8 || ldb % 8)
         return GEMM_ERR_MISALIGNED;
     return GEMM_OK;
+}
+
+gemm_status_t gemm_validate(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                            int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype)
+{
+    return validate(A, B, C, M, N, K, lda, ldb, ldc, K, K, in_dtype, out_dtype);
 }
 
 gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, gemm_plan_t *out)
@@ -363,11 +329,27 @@ gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C
                           int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int in_dtype,
                           int out_dtype, const gemm_epilogue_t *epi, hipStream_t stream)
 {
+    return gemm_run_layout(h, GEMM_K_MAJOR, GEMM_K_MAJOR, A, B, C, M, N, K, lda, ldb, ldc, in_dtype,
+                           out_dtype, epi, stream);
+}
+
+gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const void *A,
+                              const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                              int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype,
+                              const gemm_epilogue_t *epi, hipStream_t stream)
+{
     if (!h)
         return GEMM_ERR_INVALID_ARG;
-    gemm_status_t st = gemm_validate(A, B, C, M, N, K, lda, ldb, ldc, in_dtype, out_dtype);
+    if ((layout_a != GEMM_K_MAJOR && layout_a != GEMM_MN_MAJOR) ||
+        (layout_b != GEMM_K_MAJOR && layout_b != GEMM_MN_MAJOR))
+        return GEMM_ERR_INVALID_ARG;
+    const bool am = layout_a == GEMM_MN_MAJOR, bnm = layout_b == GEMM_MN_MAJOR;
+    gemm_status_t st = validate(A, B, C, M, N, K, lda, ldb, ldc, am ? M : K, bnm ? N : K,
+                                in_dtype, out_dtype);
     if (st != GEMM_OK)
         return st;
+    if ((am || bnm) && K % 8 && M && N)
+        return GEMM_ERR_UNSUPPORTED;
     if (epi) {
         if (epi->bias_along < GEMM_BIAS_NONE || epi->bias_along > GEMM_BIAS_M)
             return GEMM_ERR_INVALID_ARG;
@@ -386,7 +368,11 @@ gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C
     if (dev != h->device)
         return GEMM_ERR_INVALID_ARG;
 
-    const Plan p = make_plan(M, N, K, h->ws_bytes, h->force_cfg, h->force_splits);
+    const bool nt = !am && !bnm;
+    if (!nt && h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
+        return GEMM_ERR_UNSUPPORTED;
+    const Plan p = make_plan(M, N, K, h->ws_bytes, nt ? h->force_cfg : CFG_PP2_256x256,
+                             h->force_splits);
     if (p.splits > 1 && p.ws_bytes > h->ws_bytes)
         return GEMM_ERR_UNSUPPORTED;
     if (p.grid <= 0 || p.grid >= INT32_MAX)
@@ -429,7 +415,9 @@ gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C
         fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld\n",
                 (long long)M, (long long)N, (long long)K, c.name, p.tiles_m, p.tiles_n, p.splits,
                 p.kt_per_split, (long long)p.grid);
-    hipError_t e = c.fn[in_dtype][out_dtype](a, (unsigned)p.grid, stream);
+    const launch_fn fn = nt ? c.fn[in_dtype][out_dtype]
+                            : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
+    hipError_t e = fn(a, (unsigned)p.grid, stream);
     if (e == hipSuccess && p.splits > 1)
         e = launch_splitk_sum(a, out_dtype, stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;

@@ -1,0 +1,25 @@
+// gemm_nt_launch.hpp -- launch tables of the kernel family.  Each table lives in
+// a translation unit of its own (launch_*.hip) so the instantiations compile in
+// parallel; the host side (gemm_nt.hip) picks one entry per call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_nt_common.hpp"
+
+namespace gnt {
+
+typedef hipError_t (*launch_fn)(const KernelArgs &, unsigned grid, hipStream_t);
+// [in dtype][out dtype]; not const, so that device compilation, which gives
+// const namespace-scope tables a device copy, leaves these host-only
+typedef launch_fn LaunchTable[2][3];
+
+// kernel-template tiles (gemm_nt_kernel.hpp), in the order of their names
+extern LaunchTable kTile256x256_w4_s2, kTile256x128_w4_s3, kTile128x128_w4_s4,
+    kTile32x256_w4_s4, kTile128x128_w4_s4_kmask;
+// the 256x256 ping-pong kernels (gemm_nt_pingpong.hpp, gemm_nt_pp2.hpp); the
+// pp2 tables by operand layout: K-major A and B (NT), MN-major B, MN-major A,
+// both MN-major
+extern LaunchTable kPingpong256, kPP2_kk, kPP2_km, kPP2_mk, kPP2_mm;
+
+}  // namespace gnt

@@ -46,7 +46,7 @@
 
 namespace gnt {
 
-template <int IN, int OUT>
+template <int IN, int OUT, bool AM = false, bool BNM = false>
 __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
 {
     constexpr int BM = 256, BN = 256, BK = 64;
@@ -96,17 +96,48 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
 
     // Load number j (0..3) of the 128-row unit starting at tile row `row0` of
     // A (IS_A) or B at local slab i into LDS unit u.
+    //
+    // An operand stored MN-major (A as [K][lda], element (m, k) at A[k lda + m];
+    // B as [K][ldb]) is staged as 64 k-rows of 128 columns per unit (256-byte
+    // LDS rows): load j of wave q covers k-rows 16 j + 4 q .. +4, lane l the
+    // 16-byte chunk l % 16 of row l / 16, swizzled on the global side to
+    // logical chunk (l % 16) ^ 4 (row mod 4).  Its MFMA fragments (8
+    // consecutive k of one column) come from two transposing LDS reads.  A
+    // per-slab buffer resource ends with k-row K - 1, so k-rows past K read
+    // zeros.
+    const int mn_chunk = (lane & 15) ^ (4 * (lane >> 4));
     auto load_one = [&](auto is_a, int i, int row0, int u, int j) {
         constexpr bool IS_A = decltype(is_a)::value;
+        constexpr bool MN = IS_A ? AM : BNM;
         const int kt = kt0 + i;
-        const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * 2);
-        const bool kin = lc * 8 < p.K - kt * BK;
-        const int row = row0 + 32 * j;
-        const int rows = IS_A ? rows_a : rows_b;
-        const uint32_t ld2 = IS_A ? lda2 : ldb2;
-        const uint32_t v = (kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange;
-        load_lds16(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2,
-                   lds0 + (uint32_t)(u * UNIT + (j * 4 + q) * 1024));
+        const uint32_t dst = lds0 + (uint32_t)(u * UNIT + (j * 4 + q) * 1024);
+        if constexpr (MN) {
+            const uint16_t *X = IS_A ? p.A : p.B;
+            const int ld = IS_A ? p.lda : p.ldb;
+            const int col0 = IS_A ? m0 : n0;
+            const int rows_left = min(BK, p.K - kt * BK);
+            // the slab's k-rows as whole rows of ld elements (the operand
+            // occupies K such rows), seen from the tile's first column
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(X + (int64_t)kt * BK * ld + col0,
+                          (uint32_t)(((int64_t)rows_left * ld - col0) * 2));
+            const uint32_t ld2 = (uint32_t)ld * 2u;
+            // chunks wholly past column M (N) are not fetched: they would only
+            // feed output rows (columns) that are never stored
+            const int col = row0 + 8 * mn_chunk;
+            const uint32_t v = col < (IS_A ? rows_a : rows_b)
+                                   ? (uint32_t)(4 * q + (lane >> 4)) * ld2 + (uint32_t)col * 2u
+                                   : kOutOfRange;
+            load_lds16(rs, v, (uint32_t)(16 * j) * ld2, dst);
+        } else {
+            const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * 2);
+            const bool kin = lc * 8 < p.K - kt * BK;
+            const int row = row0 + 32 * j;
+            const int rows = IS_A ? rows_a : rows_b;
+            const uint32_t ld2 = IS_A ? lda2 : ldb2;
+            const uint32_t v = (kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange;
+            load_lds16(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2, dst);
+        }
     };
     // The eight loads a wave issues in one memory phase, n = 0..7: group 0
     // loads both halves of B(i) into B slot i % 2 (GRP = 0), group 1 both
@@ -137,17 +168,48 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
                 acc[i][j][e] = 0.0f;
 
     u32x4 af[KSTEPS][FM], bf[KSTEPS][FN];
+    // Transposing fragment read of an MN-major unit at `base`: the 8
+    // consecutive k (16 ks .. +8 (lane / 32) .. +8) of column cb + lane % 32.  Each
+    // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4 of the
+    // 8-byte pieces addressed by lanes i / 4 + 4 e (e = 0..3) of the group, so
+    // lane j addresses k-row 8 (j / 32) + 4 r + (j % 16) / 4 and columns
+    // 16 ((j / 16) % 2) + 4 (j % 4) .. +4: read r = 0 brings k .. k+3, r = 1
+    // k+4 .. k+7.  Rows 4 apart never share banks under the 4 (row mod 4) chunk
+    // swizzle, so each read takes the two-cycle minimum for its 512 bytes.
+    const int tr_kq = (lane & 15) >> 2;
+    const int tr_lp = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tr_base = (8 * (lane >> 5) + tr_kq) * 256 + 8 * (lane & 1);
+    auto read_mn = [&](const uint8_t *base, int ks, int cb) -> u32x4 {
+        const int chunk = 4 * ((cb >> 5) ^ tr_kq) + tr_lp;
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        const uint8_t *p0 = base + tr_base + (16 * ks) * 256 + chunk * 16;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s *)(uint32_t)(uintptr_t)p0);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s *)(uint32_t)(uintptr_t)(p0 + 4 * 256));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+        return (u32x4){a[0], a[1], b[0], b[1]};
+    };
     // Fragment read number r (0..23) of local slab i: ks = r / 6, then the two
     // A blocks and the four B blocks of that k16 step.
     auto read_one = [&](auto grp, int i, int r) {
         const int ks = r / 6, w = r % 6;
         const int ua = decltype(grp)::value == 0 ? U_A0 + (i & 1) : U_A1 + (i % 3);
-        const uint8_t *sa = smem + ua * UNIT + (q >> 1) * 64 * PITCH;
-        const uint8_t *sb = smem + (U_B + 2 * (i & 1) + (q & 1)) * UNIT;
-        if (w < FM)
-            af[ks][w] = *reinterpret_cast<const u32x4 *>(sa + w * 32 * PITCH + roff[ks]);
-        else
-            bf[ks][w - FM] = *reinterpret_cast<const u32x4 *>(sb + (w - FM) * 32 * PITCH + roff[ks]);
+        const int ub = U_B + 2 * (i & 1) + (q & 1);
+        if (w < FM) {
+            if constexpr (AM)
+                af[ks][w] = read_mn(smem + ua * UNIT, ks, (q >> 1) * 64 + w * 32);
+            else
+                af[ks][w] = *reinterpret_cast<const u32x4 *>(smem + ua * UNIT + (q >> 1) * 64 * PITCH +
+                                                             w * 32 * PITCH + roff[ks]);
+        } else {
+            if constexpr (BNM)
+                bf[ks][w - FM] = read_mn(smem + ub * UNIT, ks, (w - FM) * 32);
+            else
+                bf[ks][w - FM] = *reinterpret_cast<const u32x4 *>(smem + ub * UNIT + (w - FM) * 32 * PITCH +
+                                                                  roff[ks]);
+        }
     };
     // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
     // fragment reads of slab i.  Loads first: their issue is what the vector

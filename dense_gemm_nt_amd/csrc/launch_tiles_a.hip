@@ -1,0 +1,32 @@
+// Launch tables of the kernel-template tiles (gemm_nt_kernel.hpp), part one.
+#include "gemm_nt_kernel.hpp"
+#include "gemm_nt_launch.hpp"
+
+namespace gnt {
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, int IN, int OUT, bool KMASK>
+static hipError_t launch_tile(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, BK, WM, WN, ST, IN, OUT, KMASK>), dim3(grid),
+                       dim3(WM * WN * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+#define GNT_TILE_TABLE(BM, BN, BK, WM, WN, ST, KM)                                               \
+    {                                                                                            \
+        {launch_tile<BM, BN, BK, WM, WN, ST, 0, 0, KM>, launch_tile<BM, BN, BK, WM, WN, ST, 0, 1, KM>, \
+         launch_tile<BM, BN, BK, WM, WN, ST, 0, 2, KM>},                                         \
+        {launch_tile<BM, BN, BK, WM, WN, ST, 1, 0, KM>, launch_tile<BM, BN, BK, WM, WN, ST, 1, 1, KM>, \
+         launch_tile<BM, BN, BK, WM, WN, ST, 1, 2, KM>},                                         \
+    }
+
+#ifndef GNT_TILES_PART_B
+LaunchTable kTile256x256_w4_s2 = GNT_TILE_TABLE(256, 256, 64, 2, 2, 2, false);
+LaunchTable kTile256x128_w4_s3 = GNT_TILE_TABLE(256, 128, 64, 2, 2, 3, false);
+LaunchTable kTile128x128_w4_s4 = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, false);
+#else
+LaunchTable kTile32x256_w4_s4 = GNT_TILE_TABLE(32, 256, 64, 1, 4, 4, false);
+LaunchTable kTile128x128_w4_s4_kmask = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, true);
+#endif
+
+}  // namespace gnt

@@ -106,6 +106,33 @@ gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C
                           int in_dtype, int out_dtype, const gemm_epilogue_t *epi,
                           hipStream_t stream);
 
+/* Operand layouts.  The NT form keeps both operands K-major ("A Blackwell GEMM
+ * by Hand in CuTe DSL", the header of its kernel listing); "Optimizing GEMMs
+ * using tcgen05 - Part 1" ("What I am measuring") multiplies a row-major A
+ * [M][K] by a row-major B [K][N], which is B stored N-major; "Steps for Writing
+ * a Speed-of-Light GEMM kernel: Part 1" (its CuTe introduction) defines a
+ * layout as the map from a logical coordinate to a storage offset.
+ *   GEMM_K_MAJOR   A is M rows of lda elements (element (i,k) at A[i*lda + k]),
+ *                  B is N rows of ldb elements (element (j,k) at B[j*ldb + k])
+ *   GEMM_MN_MAJOR  A is K rows of lda elements (element (i,k) at A[k*lda + i]),
+ *                  B is K rows of ldb elements (element (j,k) at B[k*ldb + j])
+ * so NT = (K, K) and the row-major "A times B" with B [K][N] is (K, MN). */
+typedef enum { GEMM_K_MAJOR = 0, GEMM_MN_MAJOR = 1 } gemm_layout_t;
+
+/* gemm_run_ex for any operand layouts: C[i,j] = act(alpha sum_k a(i,k) b(j,k)
+ * + beta C_old + bias) with a, b read as layout_a / layout_b (gemm_layout_t)
+ * say; C and the epilogue as in gemm_run_ex.
+ *   lda >= K (K-major A) or >= M (MN-major A); ldb >= K or >= N likewise;
+ *   lda, ldb multiples of 8 below 2^22 and A, B 16-byte aligned.
+ * Layouts other than (K, K) need K % 8 == 0 (else GEMM_ERR_UNSUPPORTED) and run
+ * on the 256 x 256 ping-pong tile (a handle forced to another configuration
+ * returns GEMM_ERR_UNSUPPORTED); a layout value outside gemm_layout_t is
+ * GEMM_ERR_INVALID_ARG.  (K, K) is exactly gemm_run_ex. */
+gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const void *A,
+                              const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                              int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype,
+                              const gemm_epilogue_t *epi, hipStream_t stream);
+
 /* Release the handle and its workspace.  NULL is a no-op.  The caller must make
  * sure no call enqueued with this handle is still running. */
 gemm_status_t gemm_destroy(gemm_handle_t h);

@@ -127,3 +127,9 @@ def test_plan_regimes(g):
     # decode with few tiles splits K to cover the compute units
     p = g.gemm_plan(256, 8192, 8192)
     assert p["splits"] > 1 and p["workgroups"] >= 128
+
+
+def test_run_layout_rejects_null_handle_before_any_device_work(g):
+    from dense_gemm_nt_amd import _lib
+    st = _lib.lib().gemm_run_layout(None, 1, 1, A16, A16, A16, 4, 4, 8, 8, 8, 4, 0, 0, None, None)
+    assert st == 1
