@@ -101,6 +101,84 @@ def make_stored(M, N, K, layout_a="k", layout_b="k", dtype="bf16", dist="uniform
     return store(A, layout_a, lda), store(B, layout_b, ldb)
 
 
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+_FP8_TORCH = {"e4m3": "float8_e4m3fn", "e5m2": "float8_e5m2"}
+FP8_NAN = 0x7F            # a NaN code in both formats, used for padding
+
+
+def _fp8_codes(x, fmt):
+    """RNE FP8 codes (uint8) of float32 values already inside the format's range."""
+    return x.to(getattr(torch, _FP8_TORCH[fmt])).view(torch.uint8)
+
+
+def _quantize(x, fmt, mode, block_rows):
+    """(codes, scales) of float32 values: a scale per tensor or per
+    (block_rows x 128) block equal to the block's largest magnitude over the
+    format's largest finite value (1 for an all-zero block)."""
+    fmax = FP8_MAX[fmt]
+    if mode == "tensor":
+        amax = float(x.abs().max()) if x.numel() else 0.0
+        s = torch.tensor([amax / fmax if amax > 0 else 1.0], dtype=torch.float32)
+        return _fp8_codes((x / s).clamp(-fmax, fmax), fmt), s
+    rows, K = x.shape
+    nrb, nkb = -(-rows // block_rows), -(-K // 128)
+    s = torch.ones((nrb, nkb), dtype=torch.float32)
+    q = torch.empty_like(x)
+    for rb in range(nrb):
+        for kb in range(nkb):
+            blk = x[rb * block_rows:(rb + 1) * block_rows, kb * 128:(kb + 1) * 128]
+            amax = float(blk.abs().max())
+            if amax > 0:
+                s[rb, kb] = amax / fmax
+            q[rb * block_rows:(rb + 1) * block_rows, kb * 128:(kb + 1) * 128] = \
+                (blk / s[rb, kb]).clamp(-fmax, fmax)
+    return _fp8_codes(q, fmt), s
+
+
+def _pow2_scales(mode, rows, K, block_rows, salt):
+    """Powers of two from 2^-2 to 2^2, different in neighbouring blocks."""
+    if mode == "tensor":
+        return torch.tensor([2.0 ** (salt % 5 - 2)], dtype=torch.float32)
+    nrb, nkb = -(-rows // block_rows), -(-K // 128)
+    e = (torch.arange(nrb)[:, None] * 3 + torch.arange(nkb)[None, :] * 2 + salt) % 5 - 2
+    return torch.exp2(e.to(torch.float32))
+
+
+def make_fp8_operands(M, N, K, fmt_a="e4m3", fmt_b="e4m3", dist="uniform", seed=0,
+                      mode="tensor", block_m=1, lda=None, ldb=None):
+    """(A codes [M, lda], B codes [N, ldb], scales of A, scales of B).
+
+    Codes are uint8 tensors of OCP FP8 values; padding columns hold a NaN code.
+    Scales are float32: one value each ("tensor"), or [ceil(M / block_m)][ceil(K / 128)]
+    for A and [ceil(N / 128)][ceil(K / 128)] for B ("block").
+      * "uniform" / "llm": make_operands' float32 draws quantized with
+        amax scaling per tensor or per block (the recipe of blockwise FP8);
+      * "int3": integers in {-3, ..., 3} with power-of-two scales, so that every
+        partial sum is exact in FP32.
+    """
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    if lda < K or ldb < K:
+        raise ValueError("leading dimension below K")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    if dist == "int3":
+        xa = torch.randint(-3, 4, (M, K), generator=g, dtype=torch.int64).to(torch.float32)
+        xb = torch.randint(-3, 4, (N, K), generator=g, dtype=torch.int64).to(torch.float32)
+        qa, sa = _fp8_codes(xa, fmt_a), _pow2_scales(mode, M, K, block_m, 1)
+        qb, sb = _fp8_codes(xb, fmt_b), _pow2_scales(mode, N, K, 128, 3)
+    else:
+        xa = _draw((M, K), dist, "A", g)
+        xb = _draw((N, K), dist, "B", g)
+        qa, sa = _quantize(xa, fmt_a, mode, block_m)
+        qb, sb = _quantize(xb, fmt_b, mode, 128)
+    A = torch.full((M, lda), FP8_NAN, dtype=torch.uint8)
+    A[:, :K] = qa
+    B = torch.full((N, ldb), FP8_NAN, dtype=torch.uint8)
+    B[:, :K] = qb
+    return A.contiguous(), B.contiguous(), sa.contiguous(), sb.contiguous()
+
+
 def rotation_sets(M, N, K, dtype, dist, seed, count):
     """`count` independent operand pairs (seeds seed, seed+1, ...) for cold-cache timing."""
     return [make_operands(M, N, K, dtype, dist, seed + i) for i in range(count)]
