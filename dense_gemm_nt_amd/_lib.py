@@ -8,14 +8,18 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgemm_nt.so")
 
 GEMM_BF16, GEMM_FP16, GEMM_FP32 = 0, 1, 2
+GEMM_FP8_E4M3, GEMM_FP8_E5M2 = 3, 4
+FP8_FORMATS = {"e4m3": GEMM_FP8_E4M3, "e5m2": GEMM_FP8_E5M2}
+GEMM_SCALE_TENSOR, GEMM_SCALE_BLOCK = 0, 1
+SCALE_MODES = {"tensor": GEMM_SCALE_TENSOR, "block": GEMM_SCALE_BLOCK}
 GEMM_OK = 0
 GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED, GEMM_ERR_MISALIGNED = 1, 2, 3
 STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_UNSUPPORTED",
           3: "GEMM_ERR_MISALIGNED", 4: "GEMM_ERR_ALLOC", 5: "GEMM_ERR_HIP"}
 
 # Every symbol include/gemm_nt.h declares.
-EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_run_layout", "gemm_destroy",
-           "gemm_validate", "gemm_plan", "gemm_status_string")
+EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_run_layout", "gemm_run_fp8",
+           "gemm_destroy", "gemm_validate", "gemm_plan", "gemm_status_string")
 
 
 class GemmError(RuntimeError):
@@ -41,6 +45,11 @@ class GemmPlan(ctypes.Structure):
 class GemmEpilogue(ctypes.Structure):
     _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("bias", ctypes.c_void_p),
                 ("bias_along", ctypes.c_int), ("activation", ctypes.c_int)]
+
+
+class GemmFP8Scales(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("block_m", ctypes.c_int)]
 
 
 BIAS_ALONG = {"none": 0, "n": 1, "m": 2}
@@ -72,6 +81,9 @@ def lib():
     L.gemm_run_layout.argtypes = [vp, ci, ci, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci,
                                   ctypes.POINTER(GemmEpilogue), vp]
     L.gemm_run_layout.restype = ci
+    L.gemm_run_fp8.argtypes = [vp, ci, ci, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
+                               ctypes.POINTER(GemmFP8Scales), ctypes.POINTER(GemmEpilogue), vp]
+    L.gemm_run_fp8.restype = ci
     L.gemm_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci]
     L.gemm_validate.restype = ci
     L.gemm_plan.argtypes = [i64, i64, i64, ci, ci, ctypes.POINTER(GemmPlan)]
@@ -113,6 +125,21 @@ def gemm_run_layout(h, layout_a, layout_b, A, B, C, M, N, K, lda, ldb, ldc, in_d
     """Raw entry point for any operand layouts (GEMM_K_MAJOR / GEMM_MN_MAJOR each)."""
     return lib().gemm_run_layout(h, layout_a, layout_b, A, B, C, M, N, K, lda, ldb, ldc, in_dtype,
                                  out_dtype, ctypes.byref(epi) if epi is not None else None, stream)
+
+
+def gemm_run_fp8(h, a_dtype, b_dtype, A, B, C, M, N, K, lda, ldb, ldc, out_dtype, scales, epi,
+                 stream):
+    """Raw FP8 entry point: `scales` a GemmFP8Scales (or None), `epi` a GemmEpilogue or None."""
+    return lib().gemm_run_fp8(h, a_dtype, b_dtype, A, B, C, M, N, K, lda, ldb, ldc, out_dtype,
+                              ctypes.byref(scales) if scales is not None else None,
+                              ctypes.byref(epi) if epi is not None else None, stream)
+
+
+def fp8_scales(mode, a, b, block_m=1):
+    """A GemmFP8Scales; `a`, `b` are integer device addresses of FP32 scales."""
+    if mode not in SCALE_MODES:
+        raise ValueError("mode must be one of %s" % sorted(SCALE_MODES))
+    return GemmFP8Scales(SCALE_MODES[mode], a or None, b or None, int(block_m))
 
 
 def epilogue(alpha=1.0, beta=0.0, bias=0, bias_along="none", activation="none"):

@@ -61,6 +61,66 @@ class Gemm:
                                   in_dtype, out_dtype, epi, stream)
         _lib.check(st, "gemm_run_layout(%d, %d, M=%d, N=%d, K=%d)" % (layout_a, layout_b, M, N, K))
 
+    def run_raw_fp8(self, a_dtype, b_dtype, A, B, C, M, N, K, lda, ldb, ldc, out_dtype, scales,
+                    epi, stream):
+        st = _lib.gemm_run_fp8(self._h, a_dtype, b_dtype, A, B, C, M, N, K, lda, ldb, ldc,
+                               out_dtype, scales, epi, stream)
+        _lib.check(st, "gemm_run_fp8(M=%d, N=%d, K=%d)" % (M, N, K))
+
+    def fp8(self, A, B, scale_a, scale_b, fmt_a="e4m3", fmt_b="e4m3", block_m=None, out=None,
+            out_dtype=None, stream=None, alpha=1.0, beta=0.0, bias=None, bias_along="n",
+            activation="none"):
+        """C = act(alpha * sum_k sa a sb b + beta * C_old + bias) for FP8 CUDA tensors
+        A [M, K] and B [N, K] (uint8 codes or torch float8, unit stride along K).
+        scale_a / scale_b: float32 CUDA tensors with one value each (per tensor) or
+        [ceil(M / block_m), ceil(K / 128)] and [ceil(N / 128), ceil(K / 128)]
+        (blockwise; block_m 1 or 128, inferred from scale_a's shape when None)."""
+        import torch
+        if A.dim() != 2 or B.dim() != 2:
+            raise ValueError("A and B must be 2-D")
+        if beta != 0.0 and out is None:
+            raise ValueError("beta != 0 reads the prior C: pass it as `out`")
+        M, K = A.shape
+        N, K2 = B.shape
+        if K != K2:
+            raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+        if A.element_size() != 1 or B.element_size() != 1:
+            raise TypeError("A and B must hold 8-bit codes")
+        if K > 0 and (A.stride(1) != 1 or B.stride(1) != 1):
+            raise ValueError("FP8 operands need unit stride along K")
+        for sc in (scale_a, scale_b):
+            if sc.dtype != torch.float32 or not sc.is_contiguous() or sc.device != A.device:
+                raise ValueError("scales must be contiguous float32 tensors on %s" % A.device)
+        nkb = -(-K // 128)
+        if scale_a.numel() == 1 and scale_b.numel() == 1 and block_m is None:
+            mode, block_m = "tensor", 1
+        else:
+            mode = "block"
+            if block_m is None:
+                block_m = 1 if scale_a.shape[0] == M else 128
+            if tuple(scale_a.shape) != (-(-M // block_m), nkb) or \
+                    tuple(scale_b.shape) != (-(-N // 128), nkb):
+                raise ValueError("blockwise scales must be [%d, %d] and [%d, %d]"
+                                 % (-(-M // block_m), nkb, -(-N // 128), nkb))
+        if out is None:
+            out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=A.device)
+        if out.dim() != 2 or tuple(out.shape) != (M, N) or (N > 0 and out.stride(1) != 1):
+            raise ValueError("out must be [M, N] with unit column stride")
+        lda = A.stride(0) if M > 1 else max(K, A.stride(0))
+        ldb = B.stride(0) if N > 1 else max(K, B.stride(0))
+        ldc = out.stride(0) if M > 1 else max(N, out.stride(0))
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device).cuda_stream
+        epi = None
+        if not (alpha == 1.0 and beta == 0.0 and bias is None and activation == "none"):
+            epi = _lib.epilogue(alpha, beta, bias.data_ptr() if bias is not None else 0,
+                                bias_along if bias is not None else "none", activation)
+        scales = _lib.fp8_scales(mode, scale_a.data_ptr(), scale_b.data_ptr(), block_m)
+        self.run_raw_fp8(_lib.FP8_FORMATS[fmt_a], _lib.FP8_FORMATS[fmt_b], A.data_ptr(),
+                         B.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc, _code(out.dtype),
+                         scales, epi, stream)
+        return out
+
     def __call__(self, A, B, out=None, out_dtype=None, stream=None, alpha=1.0, beta=0.0,
                  bias=None, bias_along="n", activation="none"):
         """C = act(alpha * A . B^T + beta * C_old + bias) for CUDA tensors A [M, K] and
@@ -125,6 +185,14 @@ def default_handle(device_index: int) -> Gemm:
             h = Gemm()
             _handles[device_index] = h
         return h
+
+
+def gemm_fp8(A, B, scale_a, scale_b, **kw):
+    """FP8 GEMM with per-tensor or blockwise scales on A's device with the
+    per-device default handle (see Gemm.fp8)."""
+    import torch
+    with torch.cuda.device(A.device):
+        return default_handle(A.device.index).fp8(A, B, scale_a, scale_b, **kw)
 
 
 def gemm_nt(A, B, out=None, out_dtype=None, **epilogue):

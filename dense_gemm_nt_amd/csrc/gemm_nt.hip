@@ -31,7 +31,8 @@ constexpr int64_t kDefaultWorkspaceMB = 128;
 
 // The 256x256 ping-pong tile for the other operand layouts, indexed by
 // 2 * (A MN-major) + (B MN-major) - 1.
-launch_fn (*const kLayoutFns[3])[3] = {gnt::kPP2_km, gnt::kPP2_mk, gnt::kPP2_mm};
+typedef launch_fn (*LaunchTableRef)[3];   // a [2][3] launch table
+const LaunchTableRef kLayoutFns[3] = {gnt::kPP2_km, gnt::kPP2_mk, gnt::kPP2_mm};
 
 hipError_t launch_splitk_sum(const KernelArgs &a, int out_dtype, hipStream_t s)
 {
@@ -333,61 +334,48 @@ gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C
                            out_dtype, epi, stream);
 }
 
-gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const void *A,
-                              const void *B, void *C, int64_t M, int64_t N, int64_t K,
-                              int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype,
-                              const gemm_epilogue_t *epi, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+gemm_status_t check_epilogue(const gemm_epilogue_t *epi)
 {
-    if (!h)
-        return GEMM_ERR_INVALID_ARG;
-    if ((layout_a != GEMM_K_MAJOR && layout_a != GEMM_MN_MAJOR) ||
-        (layout_b != GEMM_K_MAJOR && layout_b != GEMM_MN_MAJOR))
-        return GEMM_ERR_INVALID_ARG;
-    const bool am = layout_a == GEMM_MN_MAJOR, bnm = layout_b == GEMM_MN_MAJOR;
-    gemm_status_t st = validate(A, B, C, M, N, K, lda, ldb, ldc, am ? M : K, bnm ? N : K,
-                                in_dtype, out_dtype);
-    if (st != GEMM_OK)
-        return st;
-    if ((am || bnm) && K % 8 && M && N)
-        return GEMM_ERR_UNSUPPORTED;
-    if (epi) {
-        if (epi->bias_along < GEMM_BIAS_NONE || epi->bias_along > GEMM_BIAS_M)
-            return GEMM_ERR_INVALID_ARG;
-        if (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)
-            return GEMM_ERR_INVALID_ARG;
-        if (epi->bias_along != GEMM_BIAS_NONE && (!epi->bias || (uintptr_t)epi->bias % 4))
-            return GEMM_ERR_INVALID_ARG;
-        if (!std::isfinite(epi->alpha) || !std::isfinite(epi->beta))
-            return GEMM_ERR_UNSUPPORTED;
-    }
-    if (M == 0 || N == 0)
+    if (!epi)
         return GEMM_OK;
+    if (epi->bias_along < GEMM_BIAS_NONE || epi->bias_along > GEMM_BIAS_M)
+        return GEMM_ERR_INVALID_ARG;
+    if (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)
+        return GEMM_ERR_INVALID_ARG;
+    if (epi->bias_along != GEMM_BIAS_NONE && (!epi->bias || (uintptr_t)epi->bias % 4))
+        return GEMM_ERR_INVALID_ARG;
+    if (!std::isfinite(epi->alpha) || !std::isfinite(epi->beta))
+        return GEMM_ERR_UNSUPPORTED;
+    return GEMM_OK;
+}
+
+gemm_status_t check_device(gemm_handle_t h)
+{
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess)
         return GEMM_ERR_HIP;
-    if (dev != h->device)
-        return GEMM_ERR_INVALID_ARG;
+    return dev == h->device ? GEMM_OK : GEMM_ERR_INVALID_ARG;
+}
 
-    const bool nt = !am && !bnm;
-    if (!nt && h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
-        return GEMM_ERR_UNSUPPORTED;
-    const Plan p = make_plan(M, N, K, h->ws_bytes, nt ? h->force_cfg : CFG_PP2_256x256,
-                             h->force_splits);
+// Fill the plan-, output- and epilogue-dependent fields of `a` (whose operand
+// fields the caller has set), then enqueue the kernel and, with split-K, the
+// ordered sum of the partials.
+gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn fn, void *C,
+                      int64_t M, int64_t N, int64_t K, int64_t ldc, int out_dtype,
+                      const gemm_epilogue_t *epi, hipStream_t stream)
+{
     if (p.splits > 1 && p.ws_bytes > h->ws_bytes)
         return GEMM_ERR_UNSUPPORTED;
     if (p.grid <= 0 || p.grid >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
-    const Config &c = kConfigs[p.cfg];
-
-    KernelArgs a{};
-    a.A = static_cast<const uint16_t *>(A);
-    a.B = static_cast<const uint16_t *>(B);
     a.C = C;
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.lda = (int)lda;
-    a.ldb = (int)ldb;
     a.ldc = (int)ldc;
     a.tiles_m = p.tiles_m;
     a.tiles_n = p.tiles_n;
@@ -413,14 +401,116 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     }
     if (h->log)
         fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld\n",
-                (long long)M, (long long)N, (long long)K, c.name, p.tiles_m, p.tiles_n, p.splits,
-                p.kt_per_split, (long long)p.grid);
-    const launch_fn fn = nt ? c.fn[in_dtype][out_dtype]
-                            : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
+                (long long)M, (long long)N, (long long)K, kConfigs[p.cfg].name, p.tiles_m,
+                p.tiles_n, p.splits, p.kt_per_split, (long long)p.grid);
     hipError_t e = fn(a, (unsigned)p.grid, stream);
     if (e == hipSuccess && p.splits > 1)
         e = launch_splitk_sum(a, out_dtype, stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const void *A,
+                              const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                              int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype,
+                              const gemm_epilogue_t *epi, hipStream_t stream)
+{
+    if (!h)
+        return GEMM_ERR_INVALID_ARG;
+    if ((layout_a != GEMM_K_MAJOR && layout_a != GEMM_MN_MAJOR) ||
+        (layout_b != GEMM_K_MAJOR && layout_b != GEMM_MN_MAJOR))
+        return GEMM_ERR_INVALID_ARG;
+    const bool am = layout_a == GEMM_MN_MAJOR, bnm = layout_b == GEMM_MN_MAJOR;
+    gemm_status_t st = validate(A, B, C, M, N, K, lda, ldb, ldc, am ? M : K, bnm ? N : K,
+                                in_dtype, out_dtype);
+    if (st != GEMM_OK)
+        return st;
+    if ((am || bnm) && K % 8 && M && N)
+        return GEMM_ERR_UNSUPPORTED;
+    if ((st = check_epilogue(epi)) != GEMM_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if ((st = check_device(h)) != GEMM_OK)
+        return st;
+
+    const bool nt = !am && !bnm;
+    if (!nt && h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
+        return GEMM_ERR_UNSUPPORTED;
+    const Plan p = make_plan(M, N, K, h->ws_bytes, nt ? h->force_cfg : CFG_PP2_256x256,
+                             h->force_splits);
+    KernelArgs a{};
+    a.A = static_cast<const uint16_t *>(A);
+    a.B = static_cast<const uint16_t *>(B);
+    a.lda = (int)lda;
+    a.ldb = (int)ldb;
+    const launch_fn fn = nt ? kConfigs[p.cfg].fn[in_dtype][out_dtype]
+                            : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
+    return enqueue(h, p, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
+}
+
+gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void *A,
+                           const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                           int64_t ldb, int64_t ldc, int out_dtype,
+                           const gemm_fp8_scales_t *scales, const gemm_epilogue_t *epi,
+                           hipStream_t stream)
+{
+    if (!h || !scales)
+        return GEMM_ERR_INVALID_ARG;
+    const bool fa8 = a_dtype == GEMM_FP8_E4M3 || a_dtype == GEMM_FP8_E5M2;
+    const bool fb8 = b_dtype == GEMM_FP8_E4M3 || b_dtype == GEMM_FP8_E5M2;
+    if (!fa8 || !fb8)
+        return GEMM_ERR_UNSUPPORTED;
+    // the 16-bit checks (sizes, leading dimensions, output, alignment of the
+    // bases), then the FP8 row granularity: 16 elements = 16 bytes
+    gemm_status_t st = validate(A, B, C, M, N, K, lda, ldb, ldc, K, K, GEMM_BF16, out_dtype);
+    if (st != GEMM_OK)
+        return st;
+    if (scales->mode != GEMM_SCALE_TENSOR && scales->mode != GEMM_SCALE_BLOCK)
+        return GEMM_ERR_INVALID_ARG;
+    if (scales->mode == GEMM_SCALE_BLOCK && scales->block_m != 1 && scales->block_m != 128)
+        return GEMM_ERR_INVALID_ARG;
+    if (!scales->a || !scales->b || (uintptr_t)scales->a % 4 || (uintptr_t)scales->b % 4)
+        return GEMM_ERR_INVALID_ARG;
+    if ((st = check_epilogue(epi)) != GEMM_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if (K % 16)
+        return GEMM_ERR_UNSUPPORTED;
+    if (lda % 16 || ldb % 16)
+        return GEMM_ERR_MISALIGNED;
+    const int64_t nkb = (K + 127) / 128;
+    const int64_t sfa_rows = scales->mode == GEMM_SCALE_BLOCK ? (M + scales->block_m - 1) / scales->block_m : 1;
+    const int64_t sfb_rows = scales->mode == GEMM_SCALE_BLOCK ? (N + 127) / 128 : 1;
+    const int64_t sfa_bytes = sfa_rows * (scales->mode == GEMM_SCALE_BLOCK ? nkb : 1) * 4;
+    const int64_t sfb_bytes = sfb_rows * (scales->mode == GEMM_SCALE_BLOCK ? nkb : 1) * 4;
+    if (sfa_bytes >= INT32_MAX || sfb_bytes >= INT32_MAX)
+        return GEMM_ERR_UNSUPPORTED;
+    if ((st = check_device(h)) != GEMM_OK)
+        return st;
+    if (h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
+        return GEMM_ERR_UNSUPPORTED;
+    // A slab is 128 bytes of each row: 128 FP8 values, planned as 64 16-bit ones
+    const Plan p = make_plan(M, N, K / 2, h->ws_bytes, CFG_PP2_256x256, h->force_splits);
+    KernelArgs a{};
+    a.A = static_cast<const uint16_t *>(A);
+    a.B = static_cast<const uint16_t *>(B);
+    a.lda = (int)lda;
+    a.ldb = (int)ldb;
+    a.scale_a = scales->a;
+    a.scale_b = scales->b;
+    a.sf_ld = (int)nkb;
+    a.sfa_shift = scales->block_m == 128 ? 7 : 0;
+    a.sfa_bytes = (uint32_t)sfa_bytes;
+    a.sfb_bytes = (uint32_t)sfb_bytes;
+    static LaunchTableRef const kF8[2][2] = {{gnt::kPP2_f8_e4e4, gnt::kPP2_f8_e4e5},
+                                             {gnt::kPP2_f8_e5e4, gnt::kPP2_f8_e5e5}};
+    const launch_fn fn = kF8[a_dtype == GEMM_FP8_E5M2][b_dtype == GEMM_FP8_E5M2][scales->mode][out_dtype];
+    return enqueue(h, p, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
 }
 
 }  // extern "C"

@@ -15,8 +15,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-enum : int { IN_BF16 = 0, IN_FP16 = 1 };
+// Input formats: the 16-bit ones, and the FP8 pairs IN_F8 + 2 * (A is E5M2) +
+// (B is E5M2), each operand E4M3 or E5M2 (OCP 8-bit floating point).
+enum : int { IN_BF16 = 0, IN_FP16 = 1, IN_F8 = 2 };
 enum : int { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2 };
 
 struct KernelArgs {
@@ -40,6 +43,14 @@ struct KernelArgs {
     int act;               // 0 none, 1 ReLU, 2 GELU (x * Phi(x), erf form)
     int bias_vec;          // 1 when the bias pointer is 16-byte aligned
     int epi;               // 1 when the epilogue is not the identity
+    // FP8 scales: one FP32 value each (per tensor), or blockwise: A's
+    // [ceil(M / 2^sfa_shift)][sf_ld] and B's [ceil(N / 128)][sf_ld] row-major,
+    // sf_ld = ceil(K / 128) blocks along K
+    const float *scale_a;
+    const float *scale_b;
+    int sf_ld;
+    int sfa_shift;         // log2 of the rows per A scale (0 or 7)
+    uint32_t sfa_bytes, sfb_bytes;
 };
 
 // Byte offset added to a load that must return zeros: beyond every buffer's
@@ -63,8 +74,18 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t v
                  : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr));
 }
 
-// One wave-wide 4-byte-per-lane load into LDS at lds_addr + 4 * lane.  Used to
-// pull cache lines into L2 ahead of their real load (the LDS bytes are dropped).
+// One wave-wide 4-byte-per-lane load into LDS at lds_addr + 4 * lane (lanes
+// whose offset is out of range write zeros), completion tracked with vmcnt by
+// hand like load_lds16.  Also used to pull cache lines into L2 ahead of their
+// real load, with the LDS bytes dropped (touch_lds4).
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                          uint32_t lds_addr)
+{
+    asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr));
+}
+
 __device__ __forceinline__ void touch_lds4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
                                            uint32_t lds_addr)
 {
@@ -92,6 +113,21 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c)
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// One v_mfma_f32_32x32x64_f8f6f4: the 32 k-values of a lane's row come from
+// two 16-byte fragments (k 0..15 and 16..31 of its half of the 64-deep step).
+// The B tile is the first operand, so its format goes in the first format field.
+template <int IN>
+__device__ __forceinline__ f32x16 mfma32x32x64_f8(u32x4 b0, u32x4 b1, u32x4 a0, u32x4 a1, f32x16 c)
+{
+    constexpr int fa = (IN - IN_F8) >> 1, fb = (IN - IN_F8) & 1;
+    const i32x8 x = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                     (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    const i32x8 y = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    // zero scale operands select the unscaled instruction
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, fb, fa, 0, 0, 0, 0);
 }
 
 // Swizzle key of LDS row r for a row of CH 16-byte chunks.  Depends only on

@@ -34,6 +34,27 @@
 // Output: wave w (group g = w / 4, q = w % 4) owns rows [128 g + 64 (q / 2), +64)
 // and columns [128 (q % 2), +128): 2 x 4 blocks of 32 x 32 with FP32
 // accumulators.  Requires K % 8 == 0.
+//
+// FP8 inputs ("CUTLASS Deep Dive", "FP8 and Blockwise Scaling").  A slab is
+// still 128 bytes of every row, here 128 k-values, so the loads, the ring and
+// the swizzle are the 16-bit kernel's; each MFMA (32x32x64) takes a lane's 32
+// consecutive k-values from two 16-byte fragment reads.  Per-tensor scales
+// multiply the accumulators once before the store.  Blockwise scales (one per
+// 128-deep block, per row or 128 rows of A, per 128 columns of B) are applied
+// to each slab's partial sum as it is added to the accumulators.  A lane's 16
+// accumulators of a 32x32 block share one output row and one B column block,
+// so one scale product s_i per slab; the accumulators are kept in units of
+// the current slab's s_i (acc_i = (sum over slabs j <= i of s_j P_j) / s_i),
+// which lets the MFMAs add the partial sum P_i in place: acc_i = acc_{i-1} *
+// (s_{i-1} / s_i) + P_i, and the store multiplies by the last s.  A slab whose
+// s is zero adds nothing: its A fragment is zeroed and the units are kept.
+// This needs nonzero scales to be normal FP32 numbers and sum_j s_j P_j / s_i
+// to stay in FP32 range (scale ratios along one row below about 2^80).  The
+// scales of a slab travel with its
+// operands: the waves that load A(i) also load its row scales, and wave 0 of
+// group 0 loads B(i)'s two column-block scales, by 4-byte direct-to-LDS loads
+// into slots that mirror the operand slots, so the operand waits cover them;
+// the memory phase that reads a slab's fragments reads its scales too.
 #pragma once
 
 #include <type_traits>
@@ -46,21 +67,29 @@
 
 namespace gnt {
 
-template <int IN, int OUT, bool AM = false, bool BNM = false>
+template <int IN, int OUT, bool AM = false, bool BNM = false, int SC = 0>
 __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
 {
-    constexpr int BM = 256, BN = 256, BK = 64;
-    constexpr int PITCH = BK * 2;            // 128-byte LDS rows
-    constexpr int CH = BK / 8;               // 8 chunks per row
-    constexpr int UNIT = 128 * PITCH;        // 16 KB: 128 rows of one 64-deep slab
+    constexpr bool F8 = IN >= IN_F8;
+    constexpr int ESZ = F8 ? 1 : 2;          // bytes per element
+    static_assert(!(F8 && (AM || BNM)), "FP8 operands are K-major");
+    static_assert(SC == 0 || F8, "blockwise scales are for FP8 inputs");
+    constexpr int BM = 256, BN = 256, BK = 128 / ESZ;   // k-values per slab
+    constexpr int PITCH = 128;               // 128-byte LDS rows
+    constexpr int CH = 8;                    // 16-byte chunks per row
+    constexpr int UNIT = 128 * PITCH;        // 16 KB: 128 rows of one slab
     constexpr int U_B = 0;                   // B slot s: units 2s (rows 0..127), 2s+1
     constexpr int U_A0 = 4;                  // A_0 slot s: unit 4 + s, s < 2
     constexpr int U_A1 = 6;                  // A_1 slot s: unit 6 + s, s < 3
     constexpr int UNITS = 9;
-    constexpr int FM = 2, FN = 4, KSTEPS = BK / 16;
-    static_assert(UNITS * UNIT <= 160 * 1024, "LDS budget");
+    constexpr int FM = 2, FN = 4, KSTEPS = 4;   // 16-byte fragment reads per row
+    // blockwise scales: A_0 rows in two 512-byte slots, A_1 rows in three, B's
+    // two column blocks in two 256-byte slots
+    constexpr int SA0 = UNITS * UNIT, SA1 = SA0 + 2 * 512, SB = SA1 + 3 * 512;
+    constexpr int LDS_BYTES = UNITS * UNIT + (SC ? 2 * 512 + 3 * 512 + 2 * 256 : 0);
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[UNITS * UNIT];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -78,10 +107,12 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
 
     const int rows_a = min(BM, p.M - m0);
     const int rows_b = min(BN, p.N - n0);
+    const uint8_t *Ab = reinterpret_cast<const uint8_t *>(p.A);
+    const uint8_t *Bb = reinterpret_cast<const uint8_t *>(p.B);
     const __amdgpu_buffer_rsrc_t rsA =
-        make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)rows_a * (uint32_t)p.lda * 2u);
+        make_rsrc(Ab + (int64_t)m0 * p.lda * ESZ, (uint32_t)rows_a * (uint32_t)p.lda * ESZ);
     const __amdgpu_buffer_rsrc_t rsB =
-        make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)rows_b * (uint32_t)p.ldb * 2u);
+        make_rsrc(Bb + (int64_t)n0 * p.ldb * ESZ, (uint32_t)rows_b * (uint32_t)p.ldb * ESZ);
 
     // Load slots: within a 128-row unit, load j (0..3) of wave q covers rows
     // 32 j + 8 q .. +8 (one 1 KB wave-wide load, 8 rows x 128 bytes).  The
@@ -89,7 +120,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
     // swizzled chunk are the same for every j and every unit.
     const int lrow0 = q * 8 + lane / CH;
     const int lc = (lane % CH) ^ row_key<CH>(lrow0);
-    const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+    const uint32_t lda2 = (uint32_t)p.lda * ESZ, ldb2 = (uint32_t)p.ldb * ESZ;   // row pitch, bytes
     const uint32_t voffA = (uint32_t)lrow0 * lda2 + (uint32_t)lc * 16u;
     const uint32_t voffB = (uint32_t)lrow0 * ldb2 + (uint32_t)lc * 16u;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -130,8 +161,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
                                    : kOutOfRange;
             load_lds16(rs, v, (uint32_t)(16 * j) * ld2, dst);
         } else {
-            const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * 2);
-            const bool kin = lc * 8 < p.K - kt * BK;
+            const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * ESZ);
+            const bool kin = lc * 16 < (p.K - kt * BK) * ESZ;
             const int row = row0 + 32 * j;
             const int rows = IS_A ? rows_a : rows_b;
             const uint32_t ld2 = IS_A ? lda2 : ldb2;
@@ -150,13 +181,61 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
             load_one(std::true_type{}, i, half * 128, half == 0 ? U_A0 + (i & 1) : U_A1 + (i % 3), j);
     };
 
-    int roff[KSTEPS];
-    {
-        const int r = lane & 31, h = lane >> 5;
+    // Blockwise scales of local slab i (SC == 1).  Group 1 wave q loads the
+    // row scales of tile rows 64 q .. +64 (rows of A_0 into the A_0 slot of
+    // slab i, rows of A_1 into its A_1 slot); wave 0 of group 0 loads the
+    // scales of the tile's two 128-column blocks of B.  Rows past M and blocks
+    // past N read zeros (their outputs are never stored).
+    auto scale_load = [&](auto grp, int i) {
+        if constexpr (SC == 1) {
+            const int kt = kt0 + i;
+            if constexpr (decltype(grp)::value == 1) {
+                const int m = m0 + 64 * q + lane;
+                const uint32_t v = m < p.M
+                    ? ((uint32_t)(m >> p.sfa_shift) * (uint32_t)p.sf_ld + (uint32_t)kt) * 4u
+                    : kOutOfRange;
+                const uint32_t dst = q < 2 ? SA0 + (i & 1) * 512 + q * 256
+                                           : SA1 + (i % 3) * 512 + (q - 2) * 256;
+                load_lds4(make_rsrc(p.scale_a, p.sfa_bytes), v, 0, lds0 + dst);
+            } else if (q == 0) {
+                const bool ok = lane < 2 && n0 + 128 * lane < p.N;
+                const uint32_t v = ok
+                    ? ((uint32_t)((n0 >> 7) + lane) * (uint32_t)p.sf_ld + (uint32_t)kt) * 4u
+                    : kOutOfRange;
+                load_lds4(make_rsrc(p.scale_b, p.sfb_bytes), v, 0, lds0 + SB + (i & 1) * 256);
+            }
+        }
+    };
+    // This lane's scale products for the two 32-row blocks of local slab i
+    // (read in the memory phase that reads the slab's fragments), and the
+    // units the accumulators of those blocks are held in.
+    float sblk[FM] = {1.0f, 1.0f};
+    float unit[FM] = {1.0f, 1.0f};
+    auto scale_read = [&](auto grp, int i) {
+        if constexpr (SC == 1) {
+            const float sb = *reinterpret_cast<const float *>(smem + SB + (i & 1) * 256 + (q & 1) * 4);
+            const int slot = decltype(grp)::value == 0 ? SA0 + (i & 1) * 512 : SA1 + (i % 3) * 512;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-            roff[ks] = r * PITCH + (((2 * ks + h) ^ row_key<CH>(r)) * 16);
-    }
+            for (int fm = 0; fm < FM; ++fm) {
+                const int row = (q >> 1) * 64 + fm * 32 + (lane & 31);   // within the group's half
+                sblk[fm] = *reinterpret_cast<const float *>(smem + slot + row * 4) * sb;
+            }
+        }
+    };
+
+    // Byte offset of this lane's fragment read ks within a block's rows.
+    // 16-bit: read ks holds k 16 ks + 8 h .. +8 (chunk 2 ks + h); FP8: read ks
+    // holds k 64 (ks / 2) + 32 h + 16 (ks % 2) .. +16 (chunk 4 (ks / 2) + 2 h +
+    // ks % 2).  The chunk index of read ks is the one of read 0 with bits
+    // flipped (the swizzle is an XOR), so one register carries all four.
+    const int roff0 = [&] {
+        const int r = lane & 31, h = lane >> 5;
+        return r * PITCH + (((F8 ? 2 * h : h) ^ row_key<CH>(r)) * 16);
+    }();
+    auto roff = [&](int ks) -> int {
+        const int flip = F8 ? 4 * (ks >> 1) + (ks & 1) : 2 * ks;
+        return roff0 ^ (flip * 16);
+    };
 
     f32x16 acc[FN][FM];
 #pragma unroll
@@ -202,36 +281,89 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
                 af[ks][w] = read_mn(smem + ua * UNIT, ks, (q >> 1) * 64 + w * 32);
             else
                 af[ks][w] = *reinterpret_cast<const u32x4 *>(smem + ua * UNIT + (q >> 1) * 64 * PITCH +
-                                                             w * 32 * PITCH + roff[ks]);
+                                                             w * 32 * PITCH + roff(ks));
         } else {
             if constexpr (BNM)
                 bf[ks][w - FM] = read_mn(smem + ub * UNIT, ks, (w - FM) * 32);
             else
                 bf[ks][w - FM] = *reinterpret_cast<const u32x4 *>(smem + ub * UNIT + (w - FM) * 32 * PITCH +
-                                                                  roff[ks]);
+                                                                  roff(ks));
         }
     };
     // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
     // fragment reads of slab i.  Loads first: their issue is what the vector
     // memory unit paces, and the reads overlap it.
     auto memory_phase = [&](auto grp, int i, bool has_load, int li) {
-        if (has_load)
+        if (has_load) {
 #pragma unroll
             for (int n = 0; n < 8; ++n)
                 group_load(grp, li, n);
+            scale_load(grp, li);
+        }
 #pragma unroll
         for (int r = 0; r < 24; ++r)
             read_one(grp, i, r);
+        scale_read(grp, i);
     };
     auto compute_slab = [&]() {
+        if constexpr (!F8) {
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
+            for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+                        acc[fn][fm] = mfma32x32x16<IN>(bf[ks][fn], af[ks][fm], acc[fn][fm]);
+        } else if constexpr (SC == 0) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+                        acc[fn][fm] = mfma32x32x64_f8<IN>(bf[2 * k2][fn], bf[2 * k2 + 1][fn],
+                                                          af[2 * k2][fm], af[2 * k2 + 1][fm],
+                                                          acc[fn][fm]);
+        } else {
+            float r[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const bool zero = sblk[fm] == 0.0f;
+                r[fm] = zero ? 1.0f : unit[fm] * __builtin_amdgcn_rcpf(sblk[fm]);
+                unit[fm] = zero ? unit[fm] : sblk[fm];
+                if (__builtin_amdgcn_ballot_w64(zero)) {
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ++ks)
+                        af[ks][fm] = zero ? (u32x4){0u, 0u, 0u, 0u} : af[ks][fm];
+                }
+            }
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-                    acc[fn][fm] = mfma32x32x16<IN>(bf[ks][fn], af[ks][fm], acc[fn][fm]);
+                for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[fn][fm][e] *= r[fm];
+                    acc[fn][fm] = mfma32x32x64_f8<IN>(bf[0][fn], bf[1][fn], af[0][fm], af[1][fm],
+                                                      acc[fn][fm]);
+                    acc[fn][fm] = mfma32x32x64_f8<IN>(bf[2][fn], bf[3][fn], af[2][fm], af[3][fm],
+                                                      acc[fn][fm]);
+                }
+            // Interleave: the rescale of the next block runs under the MFMAs
+            // of the current one (8 multiplies beside each MFMA).
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+#pragma unroll
+            for (int b = 0; b < FN * FM; ++b) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+        }
     };
+    // loads a group-1 wave keeps in flight across its compute phase: the
+    // eight of the next A slab and, with blockwise scales, its row scales
+    constexpr int A_INFLIGHT = SC == 1 ? 9 : 8;
     auto phase_end = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         wg_barrier();
@@ -247,16 +379,19 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
 #pragma unroll
             for (int n = 0; n < 8; ++n)
                 group_load(G0{}, 0, n);
+            scale_load(G0{}, 0);
             wait_vmcnt<0>();
         } else {
 #pragma unroll
             for (int n = 0; n < 8; ++n)
                 group_load(G1{}, 0, n);
+            scale_load(G1{}, 0);
             if (nk > 1) {
 #pragma unroll
                 for (int n = 0; n < 8; ++n)
                     group_load(G1{}, 1, n);
-                wait_vmcnt<8>();
+                scale_load(G1{}, 1);
+                wait_vmcnt<A_INFLIGHT>();
             } else {
                 wait_vmcnt<0>();
             }
@@ -290,7 +425,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
                 wait_lgkmcnt0();
                 GNT_PP2_EVENT(i, 3);
                 if (i + 2 < nk)                            // A(i+1) landed
-                    wait_vmcnt<8>();
+                    wait_vmcnt<A_INFLIGHT>();
                 else
                     wait_vmcnt<0>();
                 GNT_PP2_EVENT(i, 4);
@@ -303,6 +438,22 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
     // Epilogue (the ring is free: the last fragment read and the last load
     // completed before the loop's last barrier).  Each wave stages its own
     // 64 x 128 block in its own 16 KB of LDS.
+    if constexpr (F8) {
+        // per-tensor scales (every load of the main loop has completed), or
+        // the blockwise accumulators' last units
+        float s[FM];
+        if constexpr (SC == 0)
+            s[0] = s[1] = p.scale_a[0] * p.scale_b[0];
+        else
+            s[0] = unit[0], s[1] = unit[1];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[fn][fm][e] *= s[fm];
+    }
     const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
     uint8_t *stage = smem + wave * 16384;
     if (full && p.splits > 1 && (p.N & 3) == 0) {

@@ -43,7 +43,9 @@ typedef struct gemm_handle_s *gemm_handle_t;
 typedef enum {
     GEMM_BF16 = 0,
     GEMM_FP16 = 1,
-    GEMM_FP32 = 2
+    GEMM_FP32 = 2,
+    GEMM_FP8_E4M3 = 3, /* inputs of gemm_run_fp8 only: OCP E4M3 (bias 7, no infinities, max 448) */
+    GEMM_FP8_E5M2 = 4  /* OCP E5M2 (bias 15, IEEE-style infinities and NaNs, max 57344) */
 } gemm_dtype_t;
 
 typedef enum {
@@ -132,6 +134,41 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
                               const void *B, void *C, int64_t M, int64_t N, int64_t K,
                               int64_t lda, int64_t ldb, int64_t ldc, int in_dtype, int out_dtype,
                               const gemm_epilogue_t *epi, hipStream_t stream);
+
+/* FP8 scaling ("CUTLASS Deep Dive: From CuTe Layouts to Blackwell tcgen05",
+ * "FP8 and Blockwise Scaling": one scale per tensor, or one per (block_m,
+ * block_k) tile of A and per (block_n, block_k) tile of B, applied while
+ * accumulating).  Here block_k = block_n = 128 and the scales are FP32 device
+ * arrays, row-major:
+ *   GEMM_SCALE_TENSOR  a, b: one value each
+ *   GEMM_SCALE_BLOCK   a: [ceil(M / block_m)][ceil(K / 128)], block_m 1 or 128
+ *                      b: [ceil(N / 128)][ceil(K / 128)]
+ * Blockwise scales must be finite and either zero or normal (|s| >= 2^-126);
+ * the kernel holds each accumulator in units of the current block's scale
+ * product, so along one output row the ratio between scale products of
+ * different k-blocks must stay below about 2^80. */
+typedef enum { GEMM_SCALE_TENSOR = 0, GEMM_SCALE_BLOCK = 1 } gemm_scale_mode_t;
+typedef struct {
+    int mode;        /* gemm_scale_mode_t */
+    const float *a;  /* device pointer, 4-byte aligned */
+    const float *b;  /* device pointer, 4-byte aligned */
+    int block_m;     /* GEMM_SCALE_BLOCK: rows of A per scale, 1 or 128 */
+} gemm_fp8_scales_t;
+
+/* FP8 GEMM with scales: C[i,j] = act(alpha sum_k sa(i,k) a(i,k) sb(j,k) b(j,k)
+ * + beta C_old + bias), a and b decoded from the a_dtype / b_dtype FP8 codes
+ * (GEMM_FP8_E4M3 or GEMM_FP8_E5M2 each, K-major: A is M rows of lda bytes, B
+ * N rows of ldb bytes), sa / sb from `scales`; FP32 accumulation; C and the
+ * epilogue (NULL = identity) as in gemm_run_ex.
+ *   K % 16 == 0 and lda, ldb multiples of 16 (else GEMM_ERR_UNSUPPORTED /
+ *   GEMM_ERR_MISALIGNED); A, B 16-byte aligned; lda, ldb >= K, below 2^22.
+ *   scales NULL, a null scale pointer, an unknown mode or block_m:
+ *   GEMM_ERR_INVALID_ARG.  Runs on the 256 x 256 ping-pong tile. */
+gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void *A,
+                           const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                           int64_t ldb, int64_t ldc, int out_dtype,
+                           const gemm_fp8_scales_t *scales, const gemm_epilogue_t *epi,
+                           hipStream_t stream);
 
 /* Release the handle and its workspace.  NULL is a no-op.  The caller must make
  * sure no call enqueued with this handle is still running. */

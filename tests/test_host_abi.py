@@ -22,7 +22,7 @@ def g():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -133,3 +133,9 @@ def test_run_layout_rejects_null_handle_before_any_device_work(g):
     from dense_gemm_nt_amd import _lib
     st = _lib.lib().gemm_run_layout(None, 1, 1, A16, A16, A16, 4, 4, 8, 8, 8, 4, 0, 0, None, None)
     assert st == 1
+
+
+def test_run_fp8_rejects_null_handle_and_scales_before_any_device_work(g):
+    from dense_gemm_nt_amd import _lib
+    L = _lib.lib()
+    assert L.gemm_run_fp8(None, 3, 3, A16, A16, A16, 4, 4, 16, 16, 16, 4, 0, None, None, None) == 1
