@@ -229,6 +229,18 @@ def gemm_points(A, B, ii, jj, layout_a="k", layout_b="k", K=None, in_dtype="bf16
     return gemm_nt_points(a, b, ii, jj, in_dtype=in_dtype)
 
 
+def gemm_grouped(problems, in_dtype="bf16"):
+    """[(C_ref_g, S_g)] for a list of problems (A_g, B_g, K_g): one independent
+    NT product per group.
+
+    "CUTLASS Deep Dive: From CuTe Layouts to Blackwell tcgen05", "Grouped GEMM
+    -- MoE's workhorse": a batch of GEMMs of different shapes (one per expert)
+    computed in one launch; what each group computes is the plain product of
+    its own operands, so the oracle is that product per group.
+    """
+    return [gemm_nt(A, B, K=K, in_dtype=in_dtype) for (A, B, K) in problems]
+
+
 def decode(codes, in_dtype="bf16") -> np.ndarray:
     """Exact binary64 values of an array of 16-bit codes."""
     lib = _load()
