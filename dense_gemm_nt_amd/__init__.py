@@ -9,8 +9,8 @@ every call raises.
 from ._lib import (GEMM_BF16, GEMM_FP16, GEMM_FP32, GEMM_FP8_E4M3, GEMM_FP8_E5M2, GemmError,
                    gemm_create, gemm_destroy, gemm_plan, gemm_run, gemm_status_string,
                    gemm_validate)
-from .api import Gemm, default_handle, gemm_fp8, gemm_nt
+from .api import Gemm, default_handle, gemm_fp8, gemm_grouped, gemm_nt
 
 __all__ = ["GEMM_BF16", "GEMM_FP16", "GEMM_FP32", "GEMM_FP8_E4M3", "GEMM_FP8_E5M2", "GemmError",
-           "Gemm", "default_handle", "gemm_fp8", "gemm_nt", "gemm_create", "gemm_destroy",
+           "Gemm", "default_handle", "gemm_fp8", "gemm_grouped", "gemm_nt", "gemm_create", "gemm_destroy",
            "gemm_plan", "gemm_run", "gemm_status_string", "gemm_validate"]

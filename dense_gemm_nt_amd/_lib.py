@@ -19,7 +19,7 @@ STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_UNSUPPORTED",
 
 # Every symbol include/gemm_nt.h declares.
 EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_run_layout", "gemm_run_fp8",
-           "gemm_destroy", "gemm_validate", "gemm_plan", "gemm_status_string")
+           "gemm_run_grouped", "gemm_destroy", "gemm_validate", "gemm_plan", "gemm_status_string")
 
 
 class GemmError(RuntimeError):
@@ -50,6 +50,13 @@ class GemmEpilogue(ctypes.Structure):
 class GemmFP8Scales(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
                 ("block_m", ctypes.c_int)]
+
+
+class GemmGroupProblem(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64),
+                ("ldc", ctypes.c_int64)]
 
 
 BIAS_ALONG = {"none": 0, "n": 1, "m": 2}
@@ -84,6 +91,9 @@ def lib():
     L.gemm_run_fp8.argtypes = [vp, ci, ci, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
                                ctypes.POINTER(GemmFP8Scales), ctypes.POINTER(GemmEpilogue), vp]
     L.gemm_run_fp8.restype = ci
+    L.gemm_run_grouped.argtypes = [vp, ctypes.POINTER(GemmGroupProblem), ci, ci, ci,
+                                   ctypes.POINTER(GemmEpilogue), vp]
+    L.gemm_run_grouped.restype = ci
     L.gemm_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci]
     L.gemm_validate.restype = ci
     L.gemm_plan.argtypes = [i64, i64, i64, ci, ci, ctypes.POINTER(GemmPlan)]
@@ -133,6 +143,14 @@ def gemm_run_fp8(h, a_dtype, b_dtype, A, B, C, M, N, K, lda, ldb, ldc, out_dtype
     return lib().gemm_run_fp8(h, a_dtype, b_dtype, A, B, C, M, N, K, lda, ldb, ldc, out_dtype,
                               ctypes.byref(scales) if scales is not None else None,
                               ctypes.byref(epi) if epi is not None else None, stream)
+
+
+def gemm_run_grouped(h, problems, in_dtype, out_dtype, epi, stream):
+    """Raw grouped entry point: `problems` a list of GemmGroupProblem."""
+    arr = (GemmGroupProblem * len(problems))(*problems)
+    return lib().gemm_run_grouped(h, arr if problems else None, len(problems), in_dtype,
+                                  out_dtype, ctypes.byref(epi) if epi is not None else None,
+                                  stream)
 
 
 def fp8_scales(mode, a, b, block_m=1):

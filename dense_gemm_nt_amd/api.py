@@ -67,6 +67,63 @@ class Gemm:
                                out_dtype, scales, epi, stream)
         _lib.check(st, "gemm_run_fp8(M=%d, N=%d, K=%d)" % (M, N, K))
 
+    def grouped(self, As, Bs, outs=None, out_dtype=None, stream=None, alpha=1.0, beta=0.0,
+                biases=None, bias_along="n", activation="none"):
+        """[C_g = act(alpha * A_g . B_g^T + beta * C_g_old + bias_g)] for lists of CUDA
+        tensors A_g [M_g, K_g] and B_g [N_g, K_g] (one dtype, unit stride along K),
+        in one launch.  `outs` (needed when beta != 0) and `biases` are lists too."""
+        import torch
+        G = len(As)
+        if len(Bs) != G or (outs is not None and len(outs) != G) or \
+                (biases is not None and len(biases) != G):
+            raise ValueError("As, Bs, outs and biases must have one entry per group")
+        if beta != 0.0 and outs is None:
+            raise ValueError("beta != 0 reads the prior C: pass `outs`")
+        if G == 0:
+            return []
+        dt = As[0].dtype
+        dev = As[0].device
+        probs, res = [], []
+        for g in range(G):
+            A, B = As[g], Bs[g]
+            if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+                raise ValueError("group %d: A [M, K] and B [N, K] expected" % g)
+            if A.dtype != dt or B.dtype != dt or A.device != dev or B.device != dev:
+                raise TypeError("group %d: every operand must share dtype and device" % g)
+            M, K = A.shape
+            N = B.shape[0]
+            if K > 0 and (A.stride(1) != 1 or B.stride(1) != 1):
+                raise ValueError("group %d: operands need unit stride along K" % g)
+            C = outs[g] if outs is not None else torch.empty(
+                (M, N), dtype=out_dtype or dt, device=dev)
+            if tuple(C.shape) != (M, N) or (N > 0 and C.stride(1) != 1):
+                raise ValueError("group %d: out must be [M, N] with unit column stride" % g)
+            bias = None
+            if biases is not None and biases[g] is not None:
+                bias = biases[g]
+                want = N if bias_along == "n" else M
+                if bias.dtype != torch.float32 or bias.numel() != want or bias.stride(0) != 1:
+                    raise ValueError("group %d: bias must be %d contiguous float32 values"
+                                     % (g, want))
+            res.append(C)
+            probs.append(_lib.GemmGroupProblem(
+                A.data_ptr(), B.data_ptr(), C.data_ptr(), bias.data_ptr() if bias is not None
+                else None, M, N, K, A.stride(0) if M > 1 else max(K, A.stride(0)),
+                B.stride(0) if N > 1 else max(K, B.stride(0)),
+                C.stride(0) if M > 1 else max(N, C.stride(0))))
+        out_dt = res[0].dtype
+        if any(c.dtype != out_dt for c in res):
+            raise TypeError("every output must share one dtype")
+        with_bias = biases is not None and any(b is not None for b in biases)
+        epi = None
+        if not (alpha == 1.0 and beta == 0.0 and not with_bias and activation == "none"):
+            epi = _lib.epilogue(alpha, beta, 0, bias_along if with_bias else "none", activation)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        st = _lib.gemm_run_grouped(self._h, probs, _code(dt), _code(out_dt), epi, stream)
+        _lib.check(st, "gemm_run_grouped(%d groups)" % G)
+        return res
+
     def fp8(self, A, B, scale_a, scale_b, fmt_a="e4m3", fmt_b="e4m3", block_m=None, out=None,
             out_dtype=None, stream=None, alpha=1.0, beta=0.0, bias=None, bias_along="n",
             activation="none"):
@@ -185,6 +242,14 @@ def default_handle(device_index: int) -> Gemm:
             h = Gemm()
             _handles[device_index] = h
         return h
+
+
+def gemm_grouped(As, Bs, **kw):
+    """Grouped GEMM over lists of operands in one launch, with the per-device
+    default handle (see Gemm.grouped)."""
+    import torch
+    with torch.cuda.device(As[0].device):
+        return default_handle(As[0].device.index).grouped(As, Bs, **kw)
 
 
 def gemm_fp8(A, B, scale_a, scale_b, **kw):

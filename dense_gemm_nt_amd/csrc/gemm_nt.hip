@@ -16,6 +16,7 @@
 
 #include <cmath>
 #include <new>
+#include <vector>
 
 #include "gemm_nt.h"
 #include "gemm_nt_launch.hpp"
@@ -338,7 +339,9 @@ gemm_status_t gemm_run_ex(gemm_handle_t h, const void *A, const void *B, void *C
 
 namespace {
 
-gemm_status_t check_epilogue(const gemm_epilogue_t *epi)
+// `own_bias`: the bias pointer comes with the descriptor (false for grouped
+// launches, whose biases come with each problem).
+gemm_status_t check_epilogue(const gemm_epilogue_t *epi, bool own_bias = true)
 {
     if (!epi)
         return GEMM_OK;
@@ -346,7 +349,7 @@ gemm_status_t check_epilogue(const gemm_epilogue_t *epi)
         return GEMM_ERR_INVALID_ARG;
     if (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)
         return GEMM_ERR_INVALID_ARG;
-    if (epi->bias_along != GEMM_BIAS_NONE && (!epi->bias || (uintptr_t)epi->bias % 4))
+    if (own_bias && epi->bias_along != GEMM_BIAS_NONE && (!epi->bias || (uintptr_t)epi->bias % 4))
         return GEMM_ERR_INVALID_ARG;
     if (!std::isfinite(epi->alpha) || !std::isfinite(epi->beta))
         return GEMM_ERR_UNSUPPORTED;
@@ -450,6 +453,93 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     const launch_fn fn = nt ? kConfigs[p.cfg].fn[in_dtype][out_dtype]
                             : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
     return enqueue(h, p, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
+}
+
+gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
+                               int num_groups, int in_dtype, int out_dtype,
+                               const gemm_epilogue_t *epi, hipStream_t stream)
+{
+    if (!h || num_groups < 0 || (num_groups > 0 && !problems))
+        return GEMM_ERR_INVALID_ARG;
+    gemm_status_t st = check_epilogue(epi, false);
+    if (st != GEMM_OK)
+        return st;
+    if (epi && epi->bias)
+        return GEMM_ERR_INVALID_ARG;   // the bias of group g is problems[g].bias
+    const bool with_bias = epi && epi->bias_along != GEMM_BIAS_NONE;
+    std::vector<gnt::GroupDesc> descs;
+    descs.reserve(num_groups);
+    int64_t tiles = 0;
+    for (int g = 0; g < num_groups; ++g) {
+        const gemm_group_problem_t &q = problems[g];
+        st = validate(q.A, q.B, q.C, q.M, q.N, q.K, q.lda, q.ldb, q.ldc, q.K, q.K, in_dtype,
+                      out_dtype);
+        if (st != GEMM_OK)
+            return st;
+        if (q.K % 8)
+            return GEMM_ERR_UNSUPPORTED;
+        if (with_bias && q.M && q.N && (!q.bias || (uintptr_t)q.bias % 4))
+            return GEMM_ERR_INVALID_ARG;
+        gnt::GroupDesc d{};
+        d.A = static_cast<const uint16_t *>(q.A);
+        d.B = static_cast<const uint16_t *>(q.B);
+        d.C = q.C;
+        d.bias = with_bias ? q.bias : nullptr;
+        d.M = (int)q.M, d.N = (int)q.N, d.K = (int)q.K;
+        d.lda = (int)q.lda, d.ldb = (int)q.ldb, d.ldc = (int)q.ldc;
+        d.tiles_m = (int)cdiv(q.M, 256);
+        d.tiles_n = (int)cdiv(q.N, 256);
+        d.k_tiles = (int)cdiv(q.K, 64);
+        d.tile_start = (int)tiles;
+        const int64_t out_size = out_dtype == GEMM_FP32 ? 4 : 2;
+        const uintptr_t vec_bytes = out_dtype == GEMM_FP32 ? 16 : 8;
+        d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
+                  (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
+                  (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0);
+        descs.push_back(d);
+        tiles += (int64_t)d.tiles_m * d.tiles_n;
+        if (tiles >= INT32_MAX)
+            return GEMM_ERR_UNSUPPORTED;
+    }
+    if (tiles == 0)
+        return GEMM_OK;
+    // the problem list, then each launch position's problem index
+    const int64_t desc_bytes = (int64_t)num_groups * (int64_t)sizeof(gnt::GroupDesc);
+    const int64_t bytes = desc_bytes + tiles * 4;
+    if (bytes > h->ws_bytes)
+        return GEMM_ERR_UNSUPPORTED;
+    if ((st = check_device(h)) != GEMM_OK)
+        return st;
+    std::vector<uint8_t> host((size_t)bytes);
+    memcpy(host.data(), descs.data(), (size_t)desc_bytes);
+    int *table = reinterpret_cast<int *>(host.data() + desc_bytes);
+    for (int g = 0; g < num_groups; ++g) {
+        const int64_t n = (int64_t)descs[g].tiles_m * descs[g].tiles_n;
+        for (int64_t t = 0; t < n; ++t)
+            table[descs[g].tile_start + t] = g;
+    }
+    uint8_t *dev = reinterpret_cast<uint8_t *>(h->partials);
+    if (hipMemcpyAsync(dev, host.data(), (size_t)bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+
+    KernelArgs a{};
+    a.groups = reinterpret_cast<const gnt::GroupDesc *>(dev);
+    a.tile_group = reinterpret_cast<const int *>(dev + desc_bytes);
+    a.group_m = 4;
+    a.splits = 1;
+    a.alpha = 1.0f;
+    if (epi) {
+        a.alpha = epi->alpha;
+        a.beta = epi->beta;
+        a.bias_along = epi->bias_along;
+        a.act = epi->activation;
+        a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && a.bias_along == GEMM_BIAS_NONE &&
+                  a.act == GEMM_ACT_NONE);
+    }
+    if (h->log)
+        fprintf(stderr, "gemm_nt: grouped, %d groups, %lld tiles\n", num_groups, (long long)tiles);
+    hipError_t e = gnt::kPP2_grouped[in_dtype][out_dtype](a, (unsigned)tiles, stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void *A,

@@ -22,6 +22,23 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 enum : int { IN_BF16 = 0, IN_FP16 = 1, IN_F8 = 2 };
 enum : int { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2 };
 
+// One problem of a grouped launch ("CUTLASS Deep Dive", "Grouped GEMM -- MoE's
+// workhorse": each tile looks up its problem, then runs the usual mainloop).
+// Written by the host into device memory, one per group.
+struct GroupDesc {
+    const uint16_t *A;
+    const uint16_t *B;
+    void *C;
+    const float *bias;     // FP32 bias of this group (when the epilogue has one)
+    int M, N, K;
+    int lda, ldb, ldc;     // elements
+    int tile_start;        // the group's first position in the launch's tile list
+    int tiles_m, tiles_n, k_tiles;
+    int flags;             // GD_VEC_STORE | GD_ROWS16 | GD_BIAS_VEC
+    int pad;
+};
+enum : int { GD_VEC_STORE = 1, GD_ROWS16 = 2, GD_BIAS_VEC = 4 };
+
 struct KernelArgs {
     const uint16_t *A;
     const uint16_t *B;
@@ -51,6 +68,9 @@ struct KernelArgs {
     int sf_ld;
     int sfa_shift;         // log2 of the rows per A scale (0 or 7)
     uint32_t sfa_bytes, sfb_bytes;
+    // grouped launch: the problems, and each launch position's problem index
+    const GroupDesc *groups;
+    const int *tile_group;
 };
 
 // Byte offset added to a load that must return zeros: beyond every buffer's
@@ -141,16 +161,22 @@ __device__ __forceinline__ int row_key(int r)
         return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-// Block id -> (tile row, tile column, K split).  See the header comment.
-__device__ __forceinline__ void map_block(int bid, int G, int tiles_m, int tiles_n, int group_m,
-                                          int &tm, int &tn, int &split)
+// Launch-order position of block `bid` among G blocks: the hardware deals
+// consecutive block ids round-robin over the 8 XCDs, so renumbering gives each
+// XCD one contiguous run of positions (tiles that share operand panels in its
+// private L2).
+__device__ __forceinline__ int xcd_order(int bid, int G)
 {
     const int x = bid & 7, slot = bid >> 3;
     const int q = G >> 3, r = G & 7;
-    const int v = x * q + (x < r ? x : r) + slot;
-    const int tiles = tiles_m * tiles_n;
-    split = v / tiles;
-    const int t = v - split * tiles;
+    return x * q + (x < r ? x : r) + slot;
+}
+
+// Tile t of a tiles_m x tiles_n grid in grouped order: groups of group_m tile
+// rows, column by column within a group.
+__device__ __forceinline__ void tile_order(int t, int tiles_m, int tiles_n, int group_m, int &tm,
+                                           int &tn)
+{
     const int per_group = group_m * tiles_n;
     const int g = t / per_group;
     const int first_m = g * group_m;
@@ -158,6 +184,16 @@ __device__ __forceinline__ void map_block(int bid, int G, int tiles_m, int tiles
     const int w = t - g * per_group;
     tm = first_m + w % gsz;
     tn = w / gsz;
+}
+
+// Block id -> (tile row, tile column, K split).  See the header comment.
+__device__ __forceinline__ void map_block(int bid, int G, int tiles_m, int tiles_n, int group_m,
+                                          int &tm, int &tn, int &split)
+{
+    const int v = xcd_order(bid, G);
+    const int tiles = tiles_m * tiles_n;
+    split = v / tiles;
+    tile_order(v - split * tiles, tiles_m, tiles_n, group_m, tm, tn);
 }
 
 template <int OUT>

@@ -67,8 +67,8 @@
 
 namespace gnt {
 
-template <int IN, int OUT, bool AM = false, bool BNM = false, int SC = 0>
-__global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
+template <int IN, int OUT, bool AM = false, bool BNM = false, int SC = 0, bool GR = false>
+__global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
 {
     constexpr bool F8 = IN >= IN_F8;
     constexpr int ESZ = F8 ? 1 : 2;          // bytes per element
@@ -99,8 +99,39 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p)
     const int wm0 = group * 128 + (q >> 1) * 64;   // wave's first row within the tile
     const int wn0 = (q & 1) * 128;                 // and first column
 
+    KernelArgs p = p0;
     int tm, tn, split;
-    map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+    if constexpr (GR) {
+        // Grouped launch: this block's launch position names its problem and
+        // the tile within it; the problem's fields replace the launch's.
+        const int v = xcd_order(blockIdx.x, gridDim.x);
+        const int g = __builtin_amdgcn_readfirstlane(p0.tile_group[v]);
+        const GroupDesc *d = p0.groups + g;
+        auto u32 = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+        auto uptr = [](const void *x) {
+            const uint64_t a = (uint64_t)(uintptr_t)x;
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+            return (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+        };
+        p.A = static_cast<const uint16_t *>(uptr(d->A));
+        p.B = static_cast<const uint16_t *>(uptr(d->B));
+        p.C = uptr(d->C);
+        p.bias = static_cast<const float *>(uptr(d->bias));
+        p.M = u32(d->M), p.N = u32(d->N), p.K = u32(d->K);
+        p.lda = u32(d->lda), p.ldb = u32(d->ldb), p.ldc = u32(d->ldc);
+        p.tiles_m = u32(d->tiles_m), p.tiles_n = u32(d->tiles_n), p.k_tiles = u32(d->k_tiles);
+        p.splits = 1;
+        p.kt_per_split = p.k_tiles;
+        const int flags = u32(d->flags);
+        p.vec_store = flags & GD_VEC_STORE ? 1 : 0;
+        p.rows16 = flags & GD_ROWS16 ? 1 : 0;
+        p.bias_vec = flags & GD_BIAS_VEC ? 1 : 0;
+        split = 0;
+        tile_order(v - u32(d->tile_start), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    } else {
+        map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt0 = split * p.kt_per_split;
     const int nk = min(p.k_tiles, kt0 + p.kt_per_split) - kt0;

@@ -170,6 +170,34 @@ gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void
                            const gemm_fp8_scales_t *scales, const gemm_epilogue_t *epi,
                            hipStream_t stream);
 
+/* One problem of a grouped launch: C = A . B^T with A M rows of lda elements,
+ * B N rows of ldb, C M rows of ldc (K-major, as gemm_run). */
+typedef struct {
+    const void *A;
+    const void *B;
+    void *C;
+    const float *bias;  /* this group's FP32 bias when the epilogue has a bias axis, else unused */
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;
+} gemm_group_problem_t;
+
+/* Grouped GEMM ("CUTLASS Deep Dive: From CuTe Layouts to Blackwell tcgen05",
+ * "Grouped GEMM -- MoE's workhorse": many GEMMs of different shapes, e.g. one
+ * per expert, in one kernel launch whose tiles each look up their problem).
+ * For g < num_groups: C_g = act(alpha A_g . B_g^T + beta C_g_old + bias_g),
+ * all groups in in_dtype (BF16 or FP16) -> out_dtype with one epilogue
+ * (epi->bias must be NULL: group g's bias is problems[g].bias).
+ *   problems: host array, read before the call returns.  Each group passes the
+ *   checks of gemm_run_ex and needs K % 8 == 0 (else GEMM_ERR_UNSUPPORTED);
+ *   empty groups (M, N or K = 0; K = 0 writes the epilogue of zero) are allowed.
+ *   The problem list and a per-tile lookup table are copied into the handle's
+ *   workspace on `stream` (one call at a time per handle, as for split-K);
+ *   a list that does not fit returns GEMM_ERR_UNSUPPORTED.  Every group runs
+ *   on the 256 x 256 ping-pong tile without K splits. */
+gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
+                               int num_groups, int in_dtype, int out_dtype,
+                               const gemm_epilogue_t *epi, hipStream_t stream);
+
 /* Release the handle and its workspace.  NULL is a no-op.  The caller must make
  * sure no call enqueued with this handle is still running. */
 gemm_status_t gemm_destroy(gemm_handle_t h);

@@ -139,3 +139,8 @@ def test_run_fp8_rejects_null_handle_and_scales_before_any_device_work(g):
     from dense_gemm_nt_amd import _lib
     L = _lib.lib()
     assert L.gemm_run_fp8(None, 3, 3, A16, A16, A16, 4, 4, 16, 16, 16, 4, 0, None, None, None) == 1
+
+
+def test_run_grouped_rejects_null_handle_before_any_device_work(g):
+    from dense_gemm_nt_amd import _lib
+    assert _lib.lib().gemm_run_grouped(None, None, 0, 0, 0, None, None) == 1

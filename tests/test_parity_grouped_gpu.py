@@ -1,0 +1,171 @@
+"""Parity of the grouped GEMM (gemm_run_grouped, through the C ABI) with the
+oracle (oracle.gemm_grouped): every element of every group, on a problem list
+with ragged, tiny, empty and K = 0 groups; bitwise on small integers; the fused
+epilogue with a bias per group; a mixture-of-experts list at full size on
+sampled outputs; bitwise agreement with one launch per group; argument checks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import epilogue as oepi
+from dense_gemm_nt_amd import _lib
+from gemm_inputs import make_operands
+from tests.gpu_util import CODE, TORCH_DT, new_handle, say
+from tests.tolerance import check, check_epilogue
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+
+# (M, N, K): ragged edges, a one-row group, empty groups, K = 0, a K tail
+SHAPES = [(300, 280, 200), (1, 256, 64), (0, 100, 64), (513, 130, 136), (64, 700, 512),
+          (256, 256, 0), (7, 0, 32), (129, 33, 8)]
+
+
+def _problems(shapes, dt, dist, seed, out_dt, C_old=None, biases=None):
+    host, dev, outs = [], [], []
+    for g, (M, N, K) in enumerate(shapes):
+        A, B = make_operands(M, N, K, dt, dist, seed=seed + g)
+        host.append((A, B, K))
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        if C_old is not None:
+            Cd = C_old[g].to(DEV).clone()
+        else:
+            Cd = torch.full((M, N), float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
+        bd = biases[g].to(DEV) if biases is not None else None
+        dev.append((Ad, Bd, Cd, bd))
+        outs.append(Cd)
+    probs = [_lib.GemmGroupProblem(Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(),
+                                   bd.data_ptr() if bd is not None else None, M, N, K,
+                                   max(K, 1), max(K, 1), max(N, 1))
+             for (Ad, Bd, Cd, bd), (M, N, K) in zip(dev, shapes)]
+    return host, dev, probs, outs
+
+
+def _launch(h, probs, dt, out_dt, epi=None):
+    s = torch.cuda.current_stream(DEV)
+    st = _lib.gemm_run_grouped(h._h, probs, CODE[dt], CODE[out_dt], epi, s.cuda_stream)
+    s.synchronize()
+    return st
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("out_dt", ["bf16", "fp32"])
+def test_grouped_every_element(dt, out_dt):
+    say("case grouped %s -> %s, %d groups" % (dt, out_dt, len(SHAPES)))
+    host, dev, probs, outs = _problems(SHAPES, dt, "uniform", 11, out_dt)
+    h = new_handle()
+    assert _launch(h, probs, dt, out_dt) == _lib.GEMM_OK
+    h.close()
+    for g, ((Cr, S), C) in enumerate(zip(oracle.gemm_grouped(host, in_dtype=dt), outs)):
+        check(C.float().cpu().double().numpy(), Cr, S, out_dt, "group %d %r" % (g, SHAPES[g]))
+
+
+def test_grouped_small_integers_bitwise():
+    say("case grouped int3 bitwise")
+    host, dev, probs, outs = _problems(SHAPES, "bf16", "int3", 5, "fp32")
+    h = new_handle()
+    assert _launch(h, probs, "bf16", "fp32") == _lib.GEMM_OK
+    h.close()
+    for g, ((Cr, _), C) in enumerate(zip(oracle.gemm_grouped(host), outs)):
+        assert np.array_equal(C.cpu().double().numpy(), Cr), g
+
+
+def test_grouped_matches_one_launch_per_group_bitwise():
+    # the same tile kernel without K splits: the same MFMA order, the same bits
+    shapes = [(300, 280, 2048), (512, 512, 1024), (40, 300, 512)]
+    say("case grouped vs per-group launches")
+    host, dev, probs, outs = _problems(shapes, "bf16", "uniform", 2, "bf16")
+    h = new_handle()
+    assert _launch(h, probs, "bf16", "bf16") == _lib.GEMM_OK
+    h.close()
+    h1 = new_handle("256x256x64_w8_pp2", 1)
+    s = torch.cuda.current_stream(DEV)
+    for (Ad, Bd, Cd, _), (M, N, K) in zip(dev, shapes):
+        C1 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        h1.run_raw(Ad.data_ptr(), Bd.data_ptr(), C1.data_ptr(), M, N, K, K, K, N, 0, 0,
+                   s.cuda_stream)
+        s.synchronize()
+        assert torch.equal(C1.view(torch.int16), Cd.view(torch.int16))
+    h1.close()
+
+
+@pytest.mark.parametrize("along", ["n", "m"])
+def test_grouped_with_epilogue(along):
+    shapes = [s for s in SHAPES if s[0] and s[1]]
+    say("case grouped epilogue bias along %s" % along)
+    g = torch.Generator().manual_seed(4)
+    C_old = [(torch.rand((M, N), generator=g) * 4 - 2).to(torch.bfloat16) for M, N, _ in shapes]
+    biases = [(torch.rand(N if along == "n" else M, generator=g) * 2 - 1).to(torch.float32)
+              for M, N, _ in shapes]
+    host, dev, probs, outs = _problems(shapes, "bf16", "uniform", 9, "bf16", C_old, biases)
+    epi = _lib.epilogue(1.5, 0.25, 0, along, "gelu")
+    h = new_handle()
+    assert _launch(h, probs, "bf16", "bf16", epi) == _lib.GEMM_OK
+    h.close()
+    for i, ((Cr, S), D) in enumerate(zip(oracle.gemm_grouped(host), outs)):
+        old = C_old[i].to(torch.float64).numpy()
+        b = biases[i].numpy()
+        Dr = oepi.apply(Cr, C_old=old, alpha=1.5, beta=0.25, bias=b, bias_along=along, act="gelu")
+        aS, t = oepi.scale_of(S, C_old=old, alpha=1.5, beta=0.25, bias=b, bias_along=along)
+        check_epilogue(D.float().cpu().double().numpy(), Dr, aS, t, "bf16", "group %d" % i)
+
+
+def test_grouped_moe_sampled():
+    # eight experts of a mixture-of-experts layer: tokens per expert uneven,
+    # each expert's weight [N, K]; compared on sampled outputs
+    tokens = [1024, 3000, 512, 2048, 7, 2500, 4000, 1293]
+    N, K = 2048, 4096
+    shapes = [(m, N, K) for m in tokens]
+    say("case grouped MoE 8 experts N=%d K=%d" % (N, K))
+    host, dev, probs, outs = _problems(shapes, "bf16", "llm", 20, "bf16")
+    h = new_handle()
+    assert _launch(h, probs, "bf16", "bf16") == _lib.GEMM_OK
+    h.close()
+    rng = np.random.default_rng(1)
+    for g, ((A, B, _), C) in enumerate(zip(host, outs)):
+        M = A.shape[0]
+        ii = np.concatenate([rng.integers(0, M, 400), [0, M - 1]])
+        jj = np.concatenate([rng.integers(0, N, 400), [N - 1, 0]])
+        Cp, Sp = oracle.gemm_nt_points(A, B, ii, jj, K=K)
+        check(C.float().cpu().double().numpy()[ii, jj], Cp, Sp, "bf16", "expert %d" % g)
+
+
+def test_grouped_argument_checks():
+    h = new_handle()
+    X = torch.zeros((64, 64), dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros(64, dtype=torch.float32, device=DEV)
+    p = X.data_ptr()
+
+    def prob(M=16, N=16, K=16, lda=16, bias=None):
+        return _lib.GemmGroupProblem(p, p, p, bias, M, N, K, lda, 16, 16)
+
+    s = torch.cuda.current_stream(DEV).cuda_stream
+    run = lambda probs, epi=None: _lib.gemm_run_grouped(h._h, probs, 0, 0, epi, s)
+    assert run([prob(), prob()]) == _lib.GEMM_OK
+    assert run([]) == _lib.GEMM_OK
+    assert run([prob(), prob(K=12, lda=16)]) == _lib.GEMM_ERR_UNSUPPORTED   # K % 8
+    assert run([prob(lda=8)]) == _lib.GEMM_ERR_INVALID_ARG                 # lda < K
+    assert run([prob()], _lib.epilogue(1.0, 0.0, b.data_ptr(), "n")) == _lib.GEMM_ERR_INVALID_ARG
+    assert run([prob()], _lib.epilogue(1.0, 0.0, 0, "n")) == _lib.GEMM_ERR_INVALID_ARG  # no bias
+    assert run([prob(bias=b.data_ptr())], _lib.epilogue(1.0, 0.0, 0, "n")) == _lib.GEMM_OK
+    assert _lib.lib().gemm_run_grouped(h._h, None, 2, 0, 0, None, s) == _lib.GEMM_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    h.close()
+
+
+def test_grouped_torch_binding():
+    from dense_gemm_nt_amd import gemm_grouped
+    shapes = [(100, 300, 64), (257, 64, 128)]
+    say("case grouped torch binding")
+    As, Bs, host = [], [], []
+    for g, (M, N, K) in enumerate(shapes):
+        A, B = make_operands(M, N, K, "fp16", "uniform", seed=g)
+        host.append((A, B, K))
+        As.append(A.to(DEV))
+        Bs.append(B.to(DEV))
+    Cs = gemm_grouped(As, Bs, out_dtype=torch.float32)
+    for (Cr, S), C in zip(oracle.gemm_grouped(host, in_dtype="fp16"), Cs):
+        check(C.cpu().double().numpy(), Cr, S, "fp32", "binding")
