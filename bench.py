@@ -9,7 +9,9 @@ cache cannot hold them across steps (cold-cache numbers).  Prints one JSON line.
 
 Primary workload: M = N = K = 4096, BF16 inputs uniform on [-1, 1), FP32
 accumulation, BF16 output.  A second line item in the same JSON object reports
-the decode-regime shape M = 256, N = 28672, K = 8192 (A ~ N(0,1), B ~ N(0, 0.02^2)).
+the decode-regime shape M = 256, N = 28672, K = 8192 (A ~ N(0,1), B ~ N(0, 0.02^2)),
+and an "extensions" list times the other forms of the product (operand
+layouts, fused epilogue, FP8 with scales, grouped launch) on their workloads.
 """
 from __future__ import annotations
 
@@ -112,6 +114,125 @@ def spot_check(bufs, idx, shapes, in_dt, out_dt, dist):
     Cp, Sp = oracle.gemm_nt_points(A, B, ii, jj, K=K, in_dtype=in_dt)
     e2, w2 = check(C[ii, jj], Cp, Sp, out_dt, "bench points")
     return max(w1, w2)
+
+
+def _event_time(launch, iters, warmup, stream):
+    """Average duration of `launch()` over `iters` back-to-back calls on `stream`
+    (HIP events on that stream), after `warmup` calls."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            launch()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e-3      # seconds
+
+
+def extensions(g, iters=30, warmup=10):
+    """The other forms of the product on their own workloads: operand layouts,
+    the fused epilogue, FP8 with scales and the grouped launch.  Each is timed
+    with HIP events on its stream and spot-checked against the oracle."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle import epilogue as oepi
+    from oracle import fp8 as ofp8
+    from gemm_inputs import make_fp8_operands, make_operands, make_stored
+    from tests.tolerance import check, check_epilogue
+    from dense_gemm_nt_amd import _lib
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.Stream(device=dev)
+    sp = stream.cuda_stream
+    h = g.Gemm()
+    rng = np.random.default_rng(7)
+    res = []
+    M = N = K = 4096
+    flops = 2.0 * M * N * K
+    ii, jj = rng.integers(0, M, 1000), rng.integers(0, N, 1000)
+
+    # NN: row-major A times row-major B [K, N] (B stored N-major)
+    Xa, Xb = make_stored(M, N, K, "k", "mn", "bf16", "uniform", seed=0)
+    Ad, Bd = Xa.to(dev), Xb.to(dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t = _event_time(lambda: h.run_raw_layout(0, 1, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), M,
+                                             N, K, K, N, N, 0, 0, None, sp), iters, warmup, stream)
+    Cp, Sp = oracle.gemm_points(Xa, Xb, ii, jj, "k", "mn")
+    _, w = check(C.float().cpu().double().numpy()[ii, jj], Cp, Sp, "bf16", "NN")
+    res.append({"row": "operand layouts", "workload": "4096^3 bf16 NN (B stored [K, N])",
+                "kernel_avg_us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
+                "frac": round(flops / t / 1e12 / PEAK_TFLOPS, 4), "bound": "mfma",
+                "parity_worst_err_over_bound": round(w, 4)})
+    del Ad, Bd
+
+    # fused epilogue: bias along N + GELU
+    A, B = make_operands(M, N, K, "bf16", "uniform", seed=0)
+    Ad, Bd = A.to(dev), B.to(dev)
+    bias = (torch.rand(N, generator=torch.Generator().manual_seed(3)) * 2 - 1).float()
+    bd = bias.to(dev)
+    epi = _lib.epilogue(1.0, 0.0, bd.data_ptr(), "n", "gelu")
+    t = _event_time(lambda: h.run_raw_ex(Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), M, N, K, K,
+                                         K, N, 0, 0, epi, sp), iters, warmup, stream)
+    Cp, Sp = oracle.gemm_nt_points(A, B, ii, jj)
+    Dp = oepi.apply(Cp[None, :], bias=bias.numpy()[jj], bias_along="n", act="gelu")[0]
+    _, w = check_epilogue(C.float().cpu().double().numpy()[ii, jj], Dp, Sp,
+                          np.abs(bias.numpy()[jj].astype(np.float64)), "bf16", "epilogue")
+    res.append({"row": "fused epilogue", "workload": "4096^3 bf16, + bias[n], GELU",
+                "kernel_avg_us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
+                "frac": round(flops / t / 1e12 / PEAK_TFLOPS, 4), "bound": "mfma",
+                "parity_worst_err_over_bound": round(w, 4)})
+    del Ad, Bd, C
+
+    # FP8 E4M3 with per-tensor and with blockwise (1 x 128 / 128 x 128) scales
+    for mode in ("tensor", "block"):
+        A8, B8, sa, sb = make_fp8_operands(M, N, K, "e4m3", "e4m3", "uniform", seed=0, mode=mode,
+                                           block_m=1)
+        Ad, Bd, sad, sbd = A8.to(dev), B8.to(dev), sa.to(dev), sb.to(dev)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        sc = _lib.fp8_scales(mode, sad.data_ptr(), sbd.data_ptr(), 1)
+        t = _event_time(lambda: h.run_raw_fp8(3, 3, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), M,
+                                              N, K, K, K, N, 0, sc, None, sp), iters, warmup,
+                        stream)
+        Cp, Sp = ofp8.gemm_points(A8, B8, ii, jj, K=K, mode=mode, scale_a=sa, scale_b=sb)
+        _, w = check(C.float().cpu().double().numpy()[ii, jj], Cp, Sp, "bf16", "fp8")
+        res.append({"row": "FP8", "workload": "4096^3 e4m3 x e4m3, %s scales -> bf16" % (
+                        "per-tensor" if mode == "tensor" else "1x128 / 128x128 block"),
+                    "kernel_avg_us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
+                    "frac": round(flops / t / 1e12 / 5000.0, 4), "bound": "mfma (fp8 5.0 PF)",
+                    "parity_worst_err_over_bound": round(w, 4)})
+        del Ad, Bd, C
+
+    # grouped: 64 experts with uneven token counts, one launch
+    tokens = [64, 17, 200, 3, 90, 128, 256, 40] * 8
+    Ng, Kg = 2048, 7168
+    ops = [make_operands(m, Ng, Kg, "bf16", "llm", seed=100 + i) for i, m in enumerate(tokens)]
+    dops = [(A.to(dev), B.to(dev), torch.empty((A.shape[0], Ng), dtype=torch.bfloat16, device=dev))
+            for A, B in ops]
+    probs = [_lib.GemmGroupProblem(a.data_ptr(), b.data_ptr(), c.data_ptr(), None, a.shape[0], Ng,
+                                   Kg, Kg, Kg, Ng) for a, b, c in dops]
+    t = _event_time(lambda: _lib.gemm_run_grouped(h._h, probs, 0, 0, None, sp), iters, warmup,
+                    stream)
+    gflops = sum(2.0 * m * Ng * Kg for m in tokens)
+    worst = 0.0
+    for gi in (0, 2, 6, 11):
+        A, B = ops[gi]
+        mi = rng.integers(0, A.shape[0], 200)
+        nj = rng.integers(0, Ng, 200)
+        Cp, Sp = oracle.gemm_nt_points(A, B, mi, nj)
+        _, w = check(dops[gi][2].float().cpu().double().numpy()[mi, nj], Cp, Sp, "bf16", "grouped")
+        worst = max(worst, w)
+    res.append({"row": "grouped GEMM", "workload": "64 experts, %d tokens, N=%d K=%d bf16, one launch"
+                % (sum(tokens), Ng, Kg),
+                "kernel_avg_us": round(t * 1e6, 2), "tflops": round(gflops / t / 1e12, 1),
+                "frac": round(gflops / t / 1e12 / PEAK_TFLOPS, 4), "bound": "mfma",
+                "parity_worst_err_over_bound": round(worst, 4)})
+    h.close()
+    return res
 
 
 def cpu_baseline(shapes, in_dt, dist, target_s=10.0):
@@ -217,6 +338,10 @@ def main():
                          "traffic": traffic_for("256x28672x8192 bf16->bf16")},
             "parity_worst_err_over_bound": worst2,
         }
+
+    if not args.quick:
+        out["extensions"] = extensions(g)
+        torch.cuda.empty_cache()
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shapes, "bf16", "uniform")

@@ -82,7 +82,7 @@ def kernel_hash():
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
     for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp", "gemm_nt_pingpong.hpp",
-              "gemm_nt_pp2.hpp", "gemm_nt.hip"):
+              "gemm_nt_pp2.hpp", "gemm_nt.hip", "gemm_nt_launch.hpp", "launch_pp2.hip"):
         with open(os.path.join(root, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -122,17 +122,12 @@ def _quantize(x, fmt, mode, block_rows):
         return _fp8_codes((x / s).clamp(-fmax, fmax), fmt), s
     rows, K = x.shape
     nrb, nkb = -(-rows // block_rows), -(-K // 128)
-    s = torch.ones((nrb, nkb), dtype=torch.float32)
-    q = torch.empty_like(x)
-    for rb in range(nrb):
-        for kb in range(nkb):
-            blk = x[rb * block_rows:(rb + 1) * block_rows, kb * 128:(kb + 1) * 128]
-            amax = float(blk.abs().max())
-            if amax > 0:
-                s[rb, kb] = amax / fmax
-            q[rb * block_rows:(rb + 1) * block_rows, kb * 128:(kb + 1) * 128] = \
-                (blk / s[rb, kb]).clamp(-fmax, fmax)
-    return _fp8_codes(q, fmt), s
+    xp = torch.zeros((nrb * block_rows, nkb * 128), dtype=torch.float32)
+    xp[:rows, :K] = x
+    amax = xp.abs().reshape(nrb, block_rows, nkb, 128).amax(dim=(1, 3))
+    s = torch.where(amax > 0, amax / fmax, torch.ones_like(amax))
+    q = xp / s.repeat_interleave(block_rows, 0).repeat_interleave(128, 1)
+    return _fp8_codes(q[:rows, :K].clamp(-fmax, fmax), fmt), s.contiguous()
 
 
 def _pow2_scales(mode, rows, K, block_rows, salt):
