@@ -31,9 +31,10 @@ def kernel_hash() -> str:
     return kh()
 
 
-def traffic_for(workload_key: str):
+def traffic_for(workload_key: str, plan: dict):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the kernel as it is now (same source hash); else None."""
+    taken on the kernel as it is now (same device-source hash) and with the plan
+    this run uses (same kernel configuration and K splits); else None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
@@ -42,6 +43,9 @@ def traffic_for(workload_key: str):
         return None
     e = d.get(workload_key)
     if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    rec = e.get("plan")
+    if not rec or rec.get("name") != plan["name"] or rec.get("splits") != plan["splits"]:
         return None
     return e.get("bytes_per_launch")
 
@@ -311,7 +315,7 @@ def main():
                    "parity_worst_err_over_bound": worst},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("4096^3 bf16->bf16"),
+                     "traffic": traffic_for("4096^3 bf16->bf16", plan),
                      "kernel_avg_us": round(event_ms * 1e3, 3)},
     }
 
@@ -335,7 +339,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_TBS * 1000,
                          "unit": "GB/s", "frac": round(gbs / (HBM_TBS * 1000), 4),
                          "kernel_avg_us": round(e2 * 1e3, 3), "kernel_tflops": round(tf, 2),
-                         "traffic": traffic_for("256x28672x8192 bf16->bf16")},
+                         "traffic": traffic_for("256x28672x8192 bf16->bf16",
+                                                g.gemm_plan(*d, 0, 0))},
             "parity_worst_err_over_bound": worst2,
         }
 

@@ -455,9 +455,13 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     return enqueue(h, p, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
 }
 
-gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
-                               int num_groups, int in_dtype, int out_dtype,
-                               const gemm_epilogue_t *epi, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+gemm_status_t run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems, int num_groups,
+                          int in_dtype, int out_dtype, const gemm_epilogue_t *epi,
+                          hipStream_t stream)
 {
     if (!h || num_groups < 0 || (num_groups > 0 && !problems))
         return GEMM_ERR_INVALID_ARG;
@@ -540,6 +544,23 @@ gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *prob
         fprintf(stderr, "gemm_nt: grouped, %d groups, %lld tiles\n", num_groups, (long long)tiles);
     hipError_t e = gnt::kPP2_grouped[in_dtype][out_dtype](a, (unsigned)tiles, stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
+                               int num_groups, int in_dtype, int out_dtype,
+                               const gemm_epilogue_t *epi, hipStream_t stream)
+{
+    // the host-side problem list is built in std::vectors: no exception may
+    // cross the C boundary
+    try {
+        return run_grouped(h, problems, num_groups, in_dtype, out_dtype, epi, stream);
+    } catch (...) {
+        return GEMM_ERR_ALLOC;
+    }
 }
 
 gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void *A,

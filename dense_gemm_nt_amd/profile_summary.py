@@ -5,7 +5,7 @@
     python -m dense_gemm_nt_amd.profile_summary --counters DIR/fetch_counter_collection.csv \
         [--copy-mb 512] [--skip 2]
     python -m dense_gemm_nt_amd.profile_summary --traffic FETCH.csv WRITE.csv \
-        --key "4096^3 bf16->bf16" --update profiles/hbm_traffic.json
+        --key "4096^3 bf16->bf16" --plan 256x256x64_w8_pp2:1 --update profiles/hbm_traffic.json
 
 Counter mode averages each counter over the GEMM dispatches (after `--skip`
 warm-up launches) and, for FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scales the
@@ -76,13 +76,14 @@ def counters(path, skip):
 
 
 def kernel_hash():
-    """Same hash bench.py compares against: the kernel sources as they are now."""
+    """Same hash bench.py compares against: the device sources of the NT
+    ping-pong kernel as they are now (host-side planning is checked separately,
+    by the plan recorded beside the counters)."""
     import hashlib
     import os
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp", "gemm_nt_pingpong.hpp",
-              "gemm_nt_pp2.hpp", "gemm_nt.hip", "gemm_nt_launch.hpp", "launch_pp2.hip"):
+    for f in ("gemm_nt_common.hpp", "gemm_nt_pp2.hpp", "gemm_nt_launch.hpp", "launch_pp2.hip"):
         with open(os.path.join(root, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -119,6 +120,7 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--key", help="workload key for --traffic")
     ap.add_argument("--update", help="JSON file to add the --traffic result to")
+    ap.add_argument("--plan", help="for --traffic: the plan the counters ran, NAME:SPLITS")
     args = ap.parse_args()
     if args.traffic:
         t = traffic(args.traffic[0], args.traffic[1], args.copy_mb, args.skip)
@@ -126,6 +128,9 @@ def main():
                  "read_bytes": t["FETCH_SIZE"][0], "write_bytes": t["WRITE_SIZE"][0],
                  "fetch_calibration": t["FETCH_SIZE"][1], "write_calibration": t["WRITE_SIZE"][1],
                  "kernel": t["FETCH_SIZE"][2], "kernel_hash": kernel_hash()}
+        if args.plan:
+            name, splits = args.plan.rsplit(":", 1)
+            entry["plan"] = {"name": name, "splits": int(splits)}
         print(json.dumps({args.key: entry}, indent=1))
         if args.update:
             import os

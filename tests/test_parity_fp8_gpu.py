@@ -52,7 +52,7 @@ PAIRS = [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]
 
 @pytest.mark.parametrize("fa,fb", PAIRS)
 @pytest.mark.parametrize("mode,block_m", SCALINGS)
-@pytest.mark.parametrize("out_dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("out_dt", ["bf16", "fp16", "fp32"])
 def test_fp8_every_element(fa, fb, mode, block_m, out_dt):
     # 300 x 280: a whole 256 tile and a ragged edge; K = 400 = 3 scale blocks
     # and a 16-deep tail; leading dimensions padded (NaN codes)

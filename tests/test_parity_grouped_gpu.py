@@ -52,7 +52,7 @@ def _launch(h, probs, dt, out_dt, epi=None):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
-@pytest.mark.parametrize("out_dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("out_dt", ["bf16", "fp16", "fp32"])
 def test_grouped_every_element(dt, out_dt):
     say("case grouped %s -> %s, %d groups" % (dt, out_dt, len(SHAPES)))
     host, dev, probs, outs = _problems(SHAPES, dt, "uniform", 11, out_dt)

@@ -60,7 +60,7 @@ def _stored(M, N, K, la, lb, dt, dist, seed, pad=0):
 
 @pytest.mark.parametrize("la,lb", OTHER)
 @pytest.mark.parametrize("in_dt", ["bf16", "fp16"])
-@pytest.mark.parametrize("out_dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("out_dt", ["bf16", "fp16", "fp32"])
 def test_layout_every_element(la, lb, in_dt, out_dt):
     # 300 x 280: a whole 256 tile and a ragged edge both ways; K = 200 = 3 slabs
     # of 64 and a tail of 8; leading dimensions padded by 8 (NaN padding)
