@@ -178,6 +178,7 @@ struct gemm_handle_s {
     int64_t ws_bytes;
     int force_cfg;
     int force_splits;
+    int persistent;    // GEMM_PERSIST=1: ping-pong tiles run by 256 persistent blocks
     int log;
 };
 
@@ -275,6 +276,7 @@ gemm_status_t gemm_create(gemm_handle_t *out)
         return GEMM_ERR_ALLOC;
     h->force_cfg = -1;
     h->force_splits = -1;
+    h->persistent = 0;
     int64_t mb = kDefaultWorkspaceMB;
     if (const char *e = getenv("GEMM_WORKSPACE_MB"))
         mb = atoll(e) > 0 ? atoll(e) : mb;
@@ -287,6 +289,8 @@ gemm_status_t gemm_create(gemm_handle_t *out)
     }
     if (const char *e = getenv("GEMM_SPLITS"))
         h->force_splits = atoi(e);
+    if (const char *e = getenv("GEMM_PERSIST"))
+        h->persistent = atoi(e) != 0;
     if (const char *e = getenv("GEMM_LOG"))
         h->log = atoi(e);
     h->ws_bytes = mb << 20;
@@ -450,9 +454,14 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     a.B = static_cast<const uint16_t *>(B);
     a.lda = (int)lda;
     a.ldb = (int)ldb;
-    const launch_fn fn = nt ? kConfigs[p.cfg].fn[in_dtype][out_dtype]
-                            : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
-    return enqueue(h, p, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
+    launch_fn fn = nt ? kConfigs[p.cfg].fn[in_dtype][out_dtype]
+                      : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
+    Plan q = p;
+    if (nt && h->persistent && p.cfg == CFG_PP2_256x256 && p.grid > kNumCUs) {
+        fn = gnt::kPP2_persistent[in_dtype][out_dtype];
+        q.grid = kNumCUs;
+    }
+    return enqueue(h, q, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
 }
 
 }  // extern "C"

@@ -26,5 +26,7 @@ extern LaunchTable kPingpong256, kPP2_kk, kPP2_km, kPP2_mk, kPP2_mm;
 extern LaunchTable kPP2_f8_e4e4, kPP2_f8_e4e5, kPP2_f8_e5e4, kPP2_f8_e5e5;
 // grouped launches (16-bit inputs, K-major operands), [in dtype][out dtype]
 extern LaunchTable kPP2_grouped;
+// persistent blocks over the tiles of one problem (16-bit, K-major)
+extern LaunchTable kPP2_persistent;
 
 }  // namespace gnt

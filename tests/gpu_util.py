@@ -20,10 +20,11 @@ def say(msg):
     sys.stdout.flush()
 
 
-def new_handle(config=None, splits=None):
-    """A fresh library handle; `config` / `splits` force the plan for this handle."""
+def new_handle(config=None, splits=None, persistent=False):
+    """A fresh library handle; `config` / `splits` force the plan for this handle,
+    `persistent` runs its ping-pong tiles with persistent blocks."""
     from dense_gemm_nt_amd import Gemm
-    old = {k: os.environ.get(k) for k in ("GEMM_CONFIG", "GEMM_SPLITS")}
+    old = {k: os.environ.get(k) for k in ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_PERSIST")}
     try:
         if config:
             os.environ["GEMM_CONFIG"] = config
@@ -33,6 +34,10 @@ def new_handle(config=None, splits=None):
             os.environ["GEMM_SPLITS"] = str(splits)
         else:
             os.environ.pop("GEMM_SPLITS", None)
+        if persistent:
+            os.environ["GEMM_PERSIST"] = "1"
+        else:
+            os.environ.pop("GEMM_PERSIST", None)
         return Gemm()
     finally:
         for k, v in old.items():

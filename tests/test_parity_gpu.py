@@ -241,3 +241,23 @@ def test_misaligned_operand_is_rejected_without_launch(h):
     from dense_gemm_nt_amd import GemmError
     with pytest.raises(GemmError):
         h.run_raw(A.data_ptr() + 2, A.data_ptr(), C.data_ptr(), 8, 8, 16, 24, 24, 8, 0, 2, 0)
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(2100, 8300, 256, None), (4096, 4096, 512, 3),
+                                          (8192, 8192, 192, None)])
+def test_persistent_blocks_bitwise(M, N, K, splits):
+    # persistent blocks (256 of them, several work units each, ragged edges, K
+    # splits) run the same tile code: bitwise the grid launch's result, and the
+    # oracle's on small integers
+    say("case persistent M=%d N=%d K=%d splits=%s" % (M, N, K, splits))
+    A, B = make_operands(M, N, K, "bf16", "int3", seed=M + K)
+    hp = new_handle("256x256x64_w8_pp2", splits, persistent=True)
+    Cp = run_gpu(hp, A, B, K, "bf16", "fp32")
+    hp.close()
+    hg = new_handle("256x256x64_w8_pp2", splits)
+    Cg = run_gpu(hg, A, B, K, "bf16", "fp32")
+    hg.close()
+    assert np.array_equal(Cp, Cg)
+    rows = [0, 255, 256, M - 1]
+    Cr, _ = oracle.gemm_nt_rows(A, B, rows, K=K, in_dtype="bf16")
+    assert np.array_equal(Cp[rows], Cr)
