@@ -240,7 +240,9 @@ def extensions(g, iters=30, warmup=10):
 
 
 def cpu_baseline(shapes, in_dt, dist, target_s=10.0):
-    """The oracle as it is, on whole rows of the same workload, on this host's cores."""
+    """The oracle as it is, on whole rows of the same workload, on this host's
+    cores: about `target_s` seconds of work (more rows, or repeats of the whole
+    product once every row fits in less)."""
     import oracle
     from gemm_inputs import make_operands
     M, N, K = shapes
@@ -253,11 +255,23 @@ def cpu_baseline(shapes, in_dt, dist, target_s=10.0):
         if dt >= target_s or rows >= M:
             break
         rows = min(M, max(rows * 2, int(rows * target_s / max(dt, 1e-3) * 1.1)))
+    reps = 1
+    if dt < target_s:
+        # every row took less than the target: repeat the whole product
+        reps = max(1, int(target_s / max(dt, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.gemm_nt_rows(A, B, list(range(rows)), K=K, in_dtype=in_dt)
+        dt = (time.perf_counter() - t0) / reps
     flops = 2.0 * rows * N * K
+    if rows < M:
+        sample = "%d of %d output rows of the %dx%dx%d product (%.1f GFLOP) in %.1f s" % (
+            rows, M, M, N, K, flops / 1e9, dt)
+    else:
+        sample = "the whole %dx%dx%d product (%.1f GFLOP), %d time%s in %.1f s" % (
+            M, N, K, flops / 1e9, reps, "s" if reps > 1 else "", dt * reps)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%d of %d output rows of the %dx%dx%d product (%.1f GFLOP) in %.1f s"
-                      % (rows, M, M, N, K, flops / 1e9, dt)}
+            "kind": "oracle", "sample": sample}
 
 
 def main():
