@@ -180,6 +180,12 @@ struct gemm_handle_s {
     int force_splits;
     int persistent;    // GEMM_PERSIST=1: ping-pong tiles run by 256 persistent blocks
     int log;
+    // grouped launches: pinned staging of the problem list and an event that
+    // marks when the last copy out of it has run
+    uint8_t *staging;
+    int64_t staging_bytes;
+    hipEvent_t staged;
+    int staged_pending;
 };
 
 extern "C" {
@@ -319,6 +325,10 @@ gemm_status_t gemm_destroy(gemm_handle_t h)
         return GEMM_OK;
     gemm_status_t st = GEMM_OK;
     if (hipFree(h->partials) != hipSuccess)
+        st = GEMM_ERR_HIP;
+    if (h->staging && hipHostFree(h->staging) != hipSuccess)
+        st = GEMM_ERR_HIP;
+    if (h->staged && hipEventDestroy(h->staged) != hipSuccess)
         st = GEMM_ERR_HIP;
     delete h;
     return st;
@@ -523,17 +533,43 @@ gemm_status_t run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
         return GEMM_ERR_UNSUPPORTED;
     if ((st = check_device(h)) != GEMM_OK)
         return st;
-    std::vector<uint8_t> host((size_t)bytes);
-    memcpy(host.data(), descs.data(), (size_t)desc_bytes);
-    int *table = reinterpret_cast<int *>(host.data() + desc_bytes);
+    // Stage in pinned memory (so the copy is a true stream-ordered DMA and the
+    // call does not wait for the stream), after the previous copy out of the
+    // staging buffer has run.
+    if (h->staged_pending) {
+        if (hipEventSynchronize(h->staged) != hipSuccess)
+            return GEMM_ERR_HIP;
+        h->staged_pending = 0;
+    }
+    if (!h->staged && hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess) {
+        h->staged = nullptr;
+        return GEMM_ERR_HIP;
+    }
+    if (bytes > h->staging_bytes) {
+        if (h->staging && hipHostFree(h->staging) != hipSuccess)
+            return GEMM_ERR_HIP;
+        h->staging = nullptr;
+        h->staging_bytes = 0;
+        const int64_t want = bytes < (1 << 16) ? (1 << 16) : bytes;
+        if (hipHostMalloc((void **)&h->staging, (size_t)want, hipHostMallocDefault) != hipSuccess) {
+            h->staging = nullptr;
+            return GEMM_ERR_ALLOC;
+        }
+        h->staging_bytes = want;
+    }
+    memcpy(h->staging, descs.data(), (size_t)desc_bytes);
+    int *table = reinterpret_cast<int *>(h->staging + desc_bytes);
     for (int g = 0; g < num_groups; ++g) {
         const int64_t n = (int64_t)descs[g].tiles_m * descs[g].tiles_n;
         for (int64_t t = 0; t < n; ++t)
             table[descs[g].tile_start + t] = g;
     }
     uint8_t *dev = reinterpret_cast<uint8_t *>(h->partials);
-    if (hipMemcpyAsync(dev, host.data(), (size_t)bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    if (hipMemcpyAsync(dev, h->staging, (size_t)bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
         return GEMM_ERR_HIP;
+    if (hipEventRecord(h->staged, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    h->staged_pending = 1;
 
     KernelArgs a{};
     a.groups = reinterpret_cast<const gnt::GroupDesc *>(dev);

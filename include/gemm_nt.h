@@ -191,8 +191,10 @@ typedef struct {
  *   checks of gemm_run_ex and needs K % 8 == 0 (else GEMM_ERR_UNSUPPORTED);
  *   empty groups (M, N or K = 0; K = 0 writes the epilogue of zero) are allowed.
  *   The problem list and a per-tile lookup table are copied into the handle's
- *   workspace on `stream` (one call at a time per handle, as for split-K);
- *   a list that does not fit returns GEMM_ERR_UNSUPPORTED.  Every group runs
+ *   workspace on `stream` (one call at a time per handle, as for split-K)
+ *   through the handle's pinned staging buffer: the call waits only when the
+ *   previous grouped call's copy has not run yet.  A list that does not fit
+ *   the workspace returns GEMM_ERR_UNSUPPORTED.  Every group runs
  *   on the 256 x 256 ping-pong tile without K splits. */
 gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
                                int num_groups, int in_dtype, int out_dtype,

@@ -169,3 +169,23 @@ def test_grouped_torch_binding():
     Cs = gemm_grouped(As, Bs, out_dtype=torch.float32)
     for (Cr, S), C in zip(oracle.gemm_grouped(host, in_dtype="fp16"), Cs):
         check(C.cpu().double().numpy(), Cr, S, "fp32", "binding")
+
+
+def test_grouped_back_to_back_calls_reuse_the_staging():
+    # three grouped calls queued on one stream with no wait between them, each
+    # with its own problem list: every call reads its own list
+    h = new_handle()
+    s = torch.cuda.current_stream(DEV)
+    lists = [[(300, 280, 64), (17, 512, 128)], [(600, 40, 256)], [(1, 8, 8), (256, 256, 72), (90, 90, 16)]]
+    runs = []
+    for li, shapes in enumerate(lists):
+        say("case grouped back-to-back list %d" % li)
+        host, dev, probs, outs = _problems(shapes, "bf16", "int3", 40 + li, "fp32")
+        st = _lib.gemm_run_grouped(h._h, probs, CODE["bf16"], CODE["fp32"], None, s.cuda_stream)
+        assert st == _lib.GEMM_OK
+        runs.append((host, dev, outs))
+    s.synchronize()
+    h.close()
+    for host, _, outs in runs:
+        for (Cr, _), C in zip(oracle.gemm_grouped(host), outs):
+            assert np.array_equal(C.cpu().double().numpy(), Cr)
