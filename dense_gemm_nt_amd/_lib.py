@@ -19,7 +19,8 @@ STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_UNSUPPORTED",
 
 # Every symbol include/gemm_nt.h declares.
 EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_run_layout", "gemm_run_fp8",
-           "gemm_run_grouped", "gemm_destroy", "gemm_validate", "gemm_plan", "gemm_status_string")
+           "gemm_run_grouped", "gemm_run_grouped_fp8", "gemm_destroy", "gemm_validate",
+           "gemm_plan", "gemm_status_string")
 
 
 class GemmError(RuntimeError):
@@ -59,6 +60,14 @@ class GemmGroupProblem(ctypes.Structure):
                 ("ldc", ctypes.c_int64)]
 
 
+class GemmGroupProblemFP8(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("scale_a", ctypes.c_void_p),
+                ("scale_b", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64),
+                ("ldc", ctypes.c_int64)]
+
+
 BIAS_ALONG = {"none": 0, "n": 1, "m": 2}
 GEMM_K_MAJOR, GEMM_MN_MAJOR = 0, 1
 ACTIVATION = {"none": 0, "relu": 1, "gelu": 2}
@@ -94,6 +103,9 @@ def lib():
     L.gemm_run_grouped.argtypes = [vp, ctypes.POINTER(GemmGroupProblem), ci, ci, ci,
                                    ctypes.POINTER(GemmEpilogue), vp]
     L.gemm_run_grouped.restype = ci
+    L.gemm_run_grouped_fp8.argtypes = [vp, ci, ci, ctypes.POINTER(GemmGroupProblemFP8), ci, ci, ci,
+                                       ci, ctypes.POINTER(GemmEpilogue), vp]
+    L.gemm_run_grouped_fp8.restype = ci
     L.gemm_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci]
     L.gemm_validate.restype = ci
     L.gemm_plan.argtypes = [i64, i64, i64, ci, ci, ctypes.POINTER(GemmPlan)]
@@ -151,6 +163,16 @@ def gemm_run_grouped(h, problems, in_dtype, out_dtype, epi, stream):
     return lib().gemm_run_grouped(h, arr if problems else None, len(problems), in_dtype,
                                   out_dtype, ctypes.byref(epi) if epi is not None else None,
                                   stream)
+
+
+def gemm_run_grouped_fp8(h, a_dtype, b_dtype, problems, out_dtype, scale_mode, block_m, epi,
+                         stream):
+    """Raw grouped FP8 entry point: `problems` a list of GemmGroupProblemFP8."""
+    arr = (GemmGroupProblemFP8 * len(problems))(*problems)
+    return lib().gemm_run_grouped_fp8(h, a_dtype, b_dtype, arr if problems else None,
+                                      len(problems), out_dtype, SCALE_MODES[scale_mode],
+                                      int(block_m), ctypes.byref(epi) if epi is not None else None,
+                                      stream)
 
 
 def fp8_scales(mode, a, b, block_m=1):

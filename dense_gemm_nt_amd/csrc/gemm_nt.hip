@@ -478,6 +478,78 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
 
 namespace {
 
+// Copy a grouped launch's problem list and tile table into the workspace
+// (through the pinned staging buffer) and launch `fn` over `tiles` blocks.
+gemm_status_t stage_and_launch(gemm_handle_t h, const std::vector<gnt::GroupDesc> &descs,
+                               int64_t tiles, KernelArgs &a, launch_fn fn, hipStream_t stream)
+{
+    const int num_groups = (int)descs.size();
+    const int64_t desc_bytes = (int64_t)num_groups * (int64_t)sizeof(gnt::GroupDesc);
+    const int64_t bytes = desc_bytes + tiles * 4;
+    if (bytes > h->ws_bytes)
+        return GEMM_ERR_UNSUPPORTED;
+    gemm_status_t st = check_device(h);
+    if (st != GEMM_OK)
+        return st;
+    // Stage in pinned memory (so the copy is a true stream-ordered DMA and the
+    // call does not wait for the stream), after the previous copy out of the
+    // staging buffer has run.
+    if (h->staged_pending) {
+        if (hipEventSynchronize(h->staged) != hipSuccess)
+            return GEMM_ERR_HIP;
+        h->staged_pending = 0;
+    }
+    if (!h->staged && hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess) {
+        h->staged = nullptr;
+        return GEMM_ERR_HIP;
+    }
+    if (bytes > h->staging_bytes) {
+        if (h->staging && hipHostFree(h->staging) != hipSuccess)
+            return GEMM_ERR_HIP;
+        h->staging = nullptr;
+        h->staging_bytes = 0;
+        const int64_t want = bytes < (1 << 16) ? (1 << 16) : bytes;
+        if (hipHostMalloc((void **)&h->staging, (size_t)want, hipHostMallocDefault) != hipSuccess) {
+            h->staging = nullptr;
+            return GEMM_ERR_ALLOC;
+        }
+        h->staging_bytes = want;
+    }
+    memcpy(h->staging, descs.data(), (size_t)desc_bytes);
+    int *table = reinterpret_cast<int *>(h->staging + desc_bytes);
+    for (int g = 0; g < num_groups; ++g) {
+        const int64_t n = (int64_t)descs[g].tiles_m * descs[g].tiles_n;
+        for (int64_t t = 0; t < n; ++t)
+            table[descs[g].tile_start + t] = g;
+    }
+    uint8_t *dev = reinterpret_cast<uint8_t *>(h->partials);
+    if (hipMemcpyAsync(dev, h->staging, (size_t)bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    if (hipEventRecord(h->staged, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    h->staged_pending = 1;
+
+    a.groups = reinterpret_cast<const gnt::GroupDesc *>(dev);
+    a.tile_group = reinterpret_cast<const int *>(dev + desc_bytes);
+    a.group_m = 4;
+    a.splits = 1;
+    hipError_t e = fn(a, (unsigned)tiles, stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+void fill_group_epilogue(KernelArgs &a, const gemm_epilogue_t *epi)
+{
+    a.alpha = 1.0f;
+    if (epi) {
+        a.alpha = epi->alpha;
+        a.beta = epi->beta;
+        a.bias_along = epi->bias_along;
+        a.act = epi->activation;
+        a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && a.bias_along == GEMM_BIAS_NONE &&
+                  a.act == GEMM_ACT_NONE);
+    }
+}
+
 gemm_status_t run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems, int num_groups,
                           int in_dtype, int out_dtype, const gemm_epilogue_t *epi,
                           hipStream_t stream)
@@ -526,74 +598,116 @@ gemm_status_t run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
     }
     if (tiles == 0)
         return GEMM_OK;
-    // the problem list, then each launch position's problem index
-    const int64_t desc_bytes = (int64_t)num_groups * (int64_t)sizeof(gnt::GroupDesc);
-    const int64_t bytes = desc_bytes + tiles * 4;
-    if (bytes > h->ws_bytes)
-        return GEMM_ERR_UNSUPPORTED;
-    if ((st = check_device(h)) != GEMM_OK)
-        return st;
-    // Stage in pinned memory (so the copy is a true stream-ordered DMA and the
-    // call does not wait for the stream), after the previous copy out of the
-    // staging buffer has run.
-    if (h->staged_pending) {
-        if (hipEventSynchronize(h->staged) != hipSuccess)
-            return GEMM_ERR_HIP;
-        h->staged_pending = 0;
-    }
-    if (!h->staged && hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess) {
-        h->staged = nullptr;
-        return GEMM_ERR_HIP;
-    }
-    if (bytes > h->staging_bytes) {
-        if (h->staging && hipHostFree(h->staging) != hipSuccess)
-            return GEMM_ERR_HIP;
-        h->staging = nullptr;
-        h->staging_bytes = 0;
-        const int64_t want = bytes < (1 << 16) ? (1 << 16) : bytes;
-        if (hipHostMalloc((void **)&h->staging, (size_t)want, hipHostMallocDefault) != hipSuccess) {
-            h->staging = nullptr;
-            return GEMM_ERR_ALLOC;
-        }
-        h->staging_bytes = want;
-    }
-    memcpy(h->staging, descs.data(), (size_t)desc_bytes);
-    int *table = reinterpret_cast<int *>(h->staging + desc_bytes);
-    for (int g = 0; g < num_groups; ++g) {
-        const int64_t n = (int64_t)descs[g].tiles_m * descs[g].tiles_n;
-        for (int64_t t = 0; t < n; ++t)
-            table[descs[g].tile_start + t] = g;
-    }
-    uint8_t *dev = reinterpret_cast<uint8_t *>(h->partials);
-    if (hipMemcpyAsync(dev, h->staging, (size_t)bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-        return GEMM_ERR_HIP;
-    if (hipEventRecord(h->staged, stream) != hipSuccess)
-        return GEMM_ERR_HIP;
-    h->staged_pending = 1;
-
     KernelArgs a{};
-    a.groups = reinterpret_cast<const gnt::GroupDesc *>(dev);
-    a.tile_group = reinterpret_cast<const int *>(dev + desc_bytes);
-    a.group_m = 4;
-    a.splits = 1;
-    a.alpha = 1.0f;
-    if (epi) {
-        a.alpha = epi->alpha;
-        a.beta = epi->beta;
-        a.bias_along = epi->bias_along;
-        a.act = epi->activation;
-        a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && a.bias_along == GEMM_BIAS_NONE &&
-                  a.act == GEMM_ACT_NONE);
-    }
+    fill_group_epilogue(a, epi);
     if (h->log)
         fprintf(stderr, "gemm_nt: grouped, %d groups, %lld tiles\n", num_groups, (long long)tiles);
-    hipError_t e = gnt::kPP2_grouped[in_dtype][out_dtype](a, (unsigned)tiles, stream);
-    return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    return stage_and_launch(h, descs, tiles, a, gnt::kPP2_grouped[in_dtype][out_dtype], stream);
+}
+
+gemm_status_t run_grouped_fp8(gemm_handle_t h, int a_dtype, int b_dtype,
+                              const gemm_group_problem_fp8_t *problems, int num_groups,
+                              int out_dtype, int scale_mode, int block_m,
+                              const gemm_epilogue_t *epi, hipStream_t stream)
+{
+    if (!h || num_groups < 0 || (num_groups > 0 && !problems))
+        return GEMM_ERR_INVALID_ARG;
+    const bool fa8 = a_dtype == GEMM_FP8_E4M3 || a_dtype == GEMM_FP8_E5M2;
+    const bool fb8 = b_dtype == GEMM_FP8_E4M3 || b_dtype == GEMM_FP8_E5M2;
+    if (!fa8 || !fb8)
+        return GEMM_ERR_UNSUPPORTED;
+    if (scale_mode != GEMM_SCALE_TENSOR && scale_mode != GEMM_SCALE_BLOCK)
+        return GEMM_ERR_INVALID_ARG;
+    const bool blockwise = scale_mode == GEMM_SCALE_BLOCK;
+    if (blockwise && block_m != 1 && block_m != 128)
+        return GEMM_ERR_INVALID_ARG;
+    gemm_status_t st = check_epilogue(epi, false);
+    if (st != GEMM_OK)
+        return st;
+    if (epi && epi->bias)
+        return GEMM_ERR_INVALID_ARG;
+    const bool with_bias = epi && epi->bias_along != GEMM_BIAS_NONE;
+    std::vector<gnt::GroupDesc> descs;
+    descs.reserve(num_groups);
+    int64_t tiles = 0;
+    for (int g = 0; g < num_groups; ++g) {
+        const gemm_group_problem_fp8_t &q = problems[g];
+        st = validate(q.A, q.B, q.C, q.M, q.N, q.K, q.lda, q.ldb, q.ldc, q.K, q.K, GEMM_BF16,
+                      out_dtype);
+        if (st != GEMM_OK)
+            return st;
+        const bool empty = q.M == 0 || q.N == 0;
+        if (!empty && (!q.scale_a || !q.scale_b || (uintptr_t)q.scale_a % 4 ||
+                       (uintptr_t)q.scale_b % 4))
+            return GEMM_ERR_INVALID_ARG;
+        if (with_bias && !empty && (!q.bias || (uintptr_t)q.bias % 4))
+            return GEMM_ERR_INVALID_ARG;
+        if (!empty && q.K % 16)
+            return GEMM_ERR_UNSUPPORTED;
+        if (!empty && (q.lda % 16 || q.ldb % 16))
+            return GEMM_ERR_MISALIGNED;
+        const int64_t nkb = (q.K + 127) / 128;
+        const int64_t sfa = blockwise ? (q.M + block_m - 1) / block_m * nkb * 4 : 4;
+        const int64_t sfb = blockwise ? (q.N + 127) / 128 * nkb * 4 : 4;
+        if (sfa >= INT32_MAX || sfb >= INT32_MAX)
+            return GEMM_ERR_UNSUPPORTED;
+        gnt::GroupDesc d{};
+        d.A = static_cast<const uint16_t *>(q.A);
+        d.B = static_cast<const uint16_t *>(q.B);
+        d.C = q.C;
+        d.bias = with_bias ? q.bias : nullptr;
+        d.M = (int)q.M, d.N = (int)q.N, d.K = (int)q.K;
+        d.lda = (int)q.lda, d.ldb = (int)q.ldb, d.ldc = (int)q.ldc;
+        d.tiles_m = (int)cdiv(q.M, 256);
+        d.tiles_n = (int)cdiv(q.N, 256);
+        d.k_tiles = (int)nkb;            // a slab is 128 FP8 values
+        d.tile_start = (int)tiles;
+        d.sf_ld = (int)nkb;
+        d.scale_a = q.scale_a;
+        d.scale_b = q.scale_b;
+        d.sfa_bytes = (uint32_t)sfa;
+        d.sfb_bytes = (uint32_t)sfb;
+        const int64_t out_size = out_dtype == GEMM_FP32 ? 4 : 2;
+        const uintptr_t vec_bytes = out_dtype == GEMM_FP32 ? 16 : 8;
+        d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
+                  (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
+                  (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0);
+        descs.push_back(d);
+        tiles += (int64_t)d.tiles_m * d.tiles_n;
+        if (tiles >= INT32_MAX)
+            return GEMM_ERR_UNSUPPORTED;
+    }
+    if (tiles == 0)
+        return GEMM_OK;
+    KernelArgs a{};
+    fill_group_epilogue(a, epi);
+    a.sfa_shift = block_m == 128 ? 7 : 0;
+    static LaunchTableRef const kF8G[2][2] = {{gnt::kPP2_f8_e4e4_grouped, gnt::kPP2_f8_e4e5_grouped},
+                                              {gnt::kPP2_f8_e5e4_grouped, gnt::kPP2_f8_e5e5_grouped}};
+    const launch_fn fn =
+        kF8G[a_dtype == GEMM_FP8_E5M2][b_dtype == GEMM_FP8_E5M2][scale_mode][out_dtype];
+    if (h->log)
+        fprintf(stderr, "gemm_nt: grouped FP8, %d groups, %lld tiles\n", num_groups,
+                (long long)tiles);
+    return stage_and_launch(h, descs, tiles, a, fn, stream);
 }
 
 }  // namespace
 
 extern "C" {
+
+gemm_status_t gemm_run_grouped_fp8(gemm_handle_t h, int a_dtype, int b_dtype,
+                                   const gemm_group_problem_fp8_t *problems, int num_groups,
+                                   int out_dtype, int scale_mode, int block_m,
+                                   const gemm_epilogue_t *epi, hipStream_t stream)
+{
+    try {
+        return run_grouped_fp8(h, a_dtype, b_dtype, problems, num_groups, out_dtype, scale_mode,
+                               block_m, epi, stream);
+    } catch (...) {
+        return GEMM_ERR_ALLOC;
+    }
+}
 
 gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
                                int num_groups, int in_dtype, int out_dtype,

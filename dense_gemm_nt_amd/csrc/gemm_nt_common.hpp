@@ -35,7 +35,10 @@ struct GroupDesc {
     int tile_start;        // the group's first position in the launch's tile list
     int tiles_m, tiles_n, k_tiles;
     int flags;             // GD_VEC_STORE | GD_ROWS16 | GD_BIAS_VEC
-    int pad;
+    int sf_ld;             // FP8: k-blocks per scale row
+    const float *scale_a;  // FP8: this group's scales (per tensor or blockwise)
+    const float *scale_b;
+    uint32_t sfa_bytes, sfb_bytes;
 };
 enum : int { GD_VEC_STORE = 1, GD_ROWS16 = 2, GD_BIAS_VEC = 4 };
 

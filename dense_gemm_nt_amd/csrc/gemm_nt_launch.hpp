@@ -24,6 +24,9 @@ extern LaunchTable kPingpong256, kPP2_kk, kPP2_km, kPP2_mk, kPP2_mm;
 // FP8 inputs on the same kernel, one table per (A format, B format) with E4M3
 // = e4 and E5M2 = e5, indexed [scale mode (per tensor, blockwise)][out dtype]
 extern LaunchTable kPP2_f8_e4e4, kPP2_f8_e4e5, kPP2_f8_e5e4, kPP2_f8_e5e5;
+// and in grouped launches, [scale mode][out dtype]
+extern LaunchTable kPP2_f8_e4e4_grouped, kPP2_f8_e4e5_grouped, kPP2_f8_e5e4_grouped,
+    kPP2_f8_e5e5_grouped;
 // grouped launches (16-bit inputs, K-major operands), [in dtype][out dtype]
 extern LaunchTable kPP2_grouped;
 // persistent blocks over the tiles of one problem (16-bit, K-major)

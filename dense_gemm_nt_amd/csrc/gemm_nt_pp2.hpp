@@ -532,6 +532,13 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         p.vec_store = flags & GD_VEC_STORE ? 1 : 0;
         p.rows16 = flags & GD_ROWS16 ? 1 : 0;
         p.bias_vec = flags & GD_BIAS_VEC ? 1 : 0;
+        if constexpr (F8) {
+            p.scale_a = static_cast<const float *>(uptr(d->scale_a));
+            p.scale_b = static_cast<const float *>(uptr(d->scale_b));
+            p.sf_ld = u32(d->sf_ld);
+            p.sfa_bytes = (uint32_t)u32((int)d->sfa_bytes);
+            p.sfb_bytes = (uint32_t)u32((int)d->sfb_bytes);
+        }
         split = 0;
         tile_order(v - u32(d->tile_start), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
         tile(tm, tn, split);

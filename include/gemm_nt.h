@@ -200,6 +200,32 @@ gemm_status_t gemm_run_grouped(gemm_handle_t h, const gemm_group_problem_t *prob
                                int num_groups, int in_dtype, int out_dtype,
                                const gemm_epilogue_t *epi, hipStream_t stream);
 
+/* One FP8 problem of a grouped launch: as gemm_group_problem_t with 8-bit A
+ * and B (lda, ldb in elements = bytes) and the group's own scales, laid out as
+ * gemm_fp8_scales_t describes for the call's scale mode and block_m. */
+typedef struct {
+    const void *A;
+    const void *B;
+    void *C;
+    const float *bias;
+    const float *scale_a;
+    const float *scale_b;
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;
+} gemm_group_problem_fp8_t;
+
+/* Grouped FP8 GEMM (the grouped example of "CUTLASS Deep Dive", "Grouped GEMM
+ * -- MoE's workhorse", runs FP8 problems): gemm_run_grouped's one launch over
+ * a host list of problems, with the operands and scales of gemm_run_fp8.  One
+ * format pair, scale mode (gemm_scale_mode_t) and block_m (1 or 128, used by
+ * GEMM_SCALE_BLOCK) for the whole list; per group the checks of gemm_run_fp8
+ * (K % 16 == 0, lda and ldb multiples of 16, scales non-null and 4-byte
+ * aligned) and the staging of gemm_run_grouped. */
+gemm_status_t gemm_run_grouped_fp8(gemm_handle_t h, int a_dtype, int b_dtype,
+                                   const gemm_group_problem_fp8_t *problems, int num_groups,
+                                   int out_dtype, int scale_mode, int block_m,
+                                   const gemm_epilogue_t *epi, hipStream_t stream);
+
 /* Release the handle and its workspace.  NULL is a no-op.  The caller must make
  * sure no call enqueued with this handle is still running. */
 gemm_status_t gemm_destroy(gemm_handle_t h);

@@ -144,3 +144,8 @@ def test_run_fp8_rejects_null_handle_and_scales_before_any_device_work(g):
 def test_run_grouped_rejects_null_handle_before_any_device_work(g):
     from dense_gemm_nt_amd import _lib
     assert _lib.lib().gemm_run_grouped(None, None, 0, 0, 0, None, None) == 1
+
+
+def test_run_grouped_fp8_rejects_null_handle_before_any_device_work(g):
+    from dense_gemm_nt_amd import _lib
+    assert _lib.lib().gemm_run_grouped_fp8(None, 3, 3, None, 0, 0, 0, 1, None, None) == 1

@@ -189,3 +189,112 @@ def test_grouped_back_to_back_calls_reuse_the_staging():
     for host, _, outs in runs:
         for (Cr, _), C in zip(oracle.gemm_grouped(host), outs):
             assert np.array_equal(C.cpu().double().numpy(), Cr)
+
+
+# ---------------------------------------------------------------- FP8 groups
+
+from oracle import fp8 as ofp8  # noqa: E402
+from gemm_inputs import make_fp8_operands  # noqa: E402
+
+F8_SHAPES = [(300, 280, 400), (1, 256, 128), (0, 64, 128), (513, 130, 144), (64, 700, 512),
+             (256, 256, 16)]
+F8_CODE = {"e4m3": _lib.GEMM_FP8_E4M3, "e5m2": _lib.GEMM_FP8_E5M2}
+
+
+def _f8_problems(shapes, fa, fb, mode, block_m, dist, seed, out_dt):
+    host, keep, probs = [], [], []
+    for g, (M, N, K) in enumerate(shapes):
+        A, B, sa, sb = make_fp8_operands(M, N, K, fa, fb, dist, seed=seed + g, mode=mode,
+                                         block_m=block_m)
+        host.append((A, B, sa, sb, K))
+        Ad, Bd, sad, sbd = A.to(DEV), B.to(DEV), sa.to(DEV), sb.to(DEV)
+        Cd = torch.full((M, N), float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
+        keep.append((Ad, Bd, sad, sbd, Cd))
+        probs.append(_lib.GemmGroupProblemFP8(Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), None,
+                                              sad.data_ptr(), sbd.data_ptr(), M, N, K,
+                                              max(K, 1), max(K, 1), max(N, 1)))
+    return host, keep, probs
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3")])
+@pytest.mark.parametrize("mode,block_m", [("tensor", 1), ("block", 1), ("block", 128)])
+def test_grouped_fp8_every_element(fa, fb, mode, block_m):
+    say("case grouped fp8 %s x %s %s/%d" % (fa, fb, mode, block_m))
+    host, keep, probs = _f8_problems(F8_SHAPES, fa, fb, mode, block_m, "uniform", 60, "bf16")
+    h = new_handle()
+    s = torch.cuda.current_stream(DEV)
+    st = _lib.gemm_run_grouped_fp8(h._h, F8_CODE[fa], F8_CODE[fb], probs, CODE["bf16"], mode,
+                                   block_m, None, s.cuda_stream)
+    s.synchronize()
+    h.close()
+    assert st == _lib.GEMM_OK
+    for g, ((A, B, sa, sb, K), k) in enumerate(zip(host, keep)):
+        Cr, S = ofp8.gemm(A, B, K=K, fmt_a=fa, fmt_b=fb, mode=mode, scale_a=sa, scale_b=sb,
+                          block_m=block_m)
+        check(k[4].float().cpu().double().numpy(), Cr, S, "bf16", "fp8 group %d" % g)
+
+
+@pytest.mark.parametrize("mode,block_m", [("tensor", 1), ("block", 1), ("block", 128)])
+def test_grouped_fp8_small_integers_bitwise_and_equal_to_single_launches(mode, block_m):
+    say("case grouped fp8 int3 %s/%d" % (mode, block_m))
+    host, keep, probs = _f8_problems(F8_SHAPES, "e4m3", "e5m2", mode, block_m, "int3", 70, "fp32")
+    h = new_handle()
+    s = torch.cuda.current_stream(DEV)
+    st = _lib.gemm_run_grouped_fp8(h._h, F8_CODE["e4m3"], F8_CODE["e5m2"], probs, CODE["fp32"],
+                                   mode, block_m, None, s.cuda_stream)
+    s.synchronize()
+    h.close()
+    assert st == _lib.GEMM_OK
+    h1 = new_handle("256x256x64_w8_pp2", 1)
+    for g, ((A, B, sa, sb, K), (Ad, Bd, sad, sbd, Cd)) in enumerate(zip(host, keep)):
+        Cr, _ = ofp8.gemm(A, B, K=K, fmt_a="e4m3", fmt_b="e5m2", mode=mode, scale_a=sa,
+                          scale_b=sb, block_m=block_m)
+        C = Cd.cpu().double().numpy()
+        assert np.array_equal(C, Cr), g
+        M, N = Cd.shape
+        if M and N and K:
+            C1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            sc = _lib.fp8_scales(mode, sad.data_ptr(), sbd.data_ptr(), block_m)
+            h1.run_raw_fp8(F8_CODE["e4m3"], F8_CODE["e5m2"], Ad.data_ptr(), Bd.data_ptr(),
+                           C1.data_ptr(), M, N, K, K, K, N, CODE["fp32"], sc, None, s.cuda_stream)
+            s.synchronize()
+            assert torch.equal(C1, Cd), g
+    h1.close()
+
+
+def test_grouped_fp8_with_epilogue_and_checks():
+    shapes = [(300, 280, 256), (64, 512, 128)]
+    say("case grouped fp8 epilogue")
+    host, keep, probs = _f8_problems(shapes, "e4m3", "e4m3", "block", 1, "uniform", 80, "bf16")
+    g = torch.Generator().manual_seed(5)
+    biases = [(torch.rand(N, generator=g) * 2 - 1).float() for _, N, _ in shapes]
+    bds = [b.to(DEV) for b in biases]
+    for p, bd in zip(probs, bds):
+        p.bias = bd.data_ptr()
+    h = new_handle()
+    s = torch.cuda.current_stream(DEV)
+    epi = _lib.epilogue(0.5, 0.0, 0, "n", "relu")
+    st = _lib.gemm_run_grouped_fp8(h._h, F8_CODE["e4m3"], F8_CODE["e4m3"], probs, CODE["bf16"],
+                                   "block", 1, epi, s.cuda_stream)
+    s.synchronize()
+    assert st == _lib.GEMM_OK
+    for (A, B, sa, sb, K), k, b in zip(host, keep, biases):
+        Cr, S = ofp8.gemm(A, B, K=K, mode="block", scale_a=sa, scale_b=sb, block_m=1)
+        Dr = oepi.apply(Cr, alpha=0.5, bias=b.numpy(), bias_along="n", act="relu")
+        aS, t = oepi.scale_of(S, alpha=0.5, bias=b.numpy(), bias_along="n")
+        check_epilogue(k[4].float().cpu().double().numpy(), Dr, aS, t, "bf16", "fp8 group epi")
+    # argument checks: K % 16, a null scale, an unknown block_m, a 16-bit format
+    bad = _lib.GemmGroupProblemFP8(*[getattr(probs[0], f) for f, _ in probs[0]._fields_])
+    bad.K = 24
+    assert _lib.gemm_run_grouped_fp8(h._h, 3, 3, [bad], 0, "block", 1, None,
+                                     s.cuda_stream) == _lib.GEMM_ERR_UNSUPPORTED
+    bad = _lib.GemmGroupProblemFP8(*[getattr(probs[0], f) for f, _ in probs[0]._fields_])
+    bad.scale_a = None
+    assert _lib.gemm_run_grouped_fp8(h._h, 3, 3, [bad], 0, "tensor", 1, None,
+                                     s.cuda_stream) == _lib.GEMM_ERR_INVALID_ARG
+    assert _lib.gemm_run_grouped_fp8(h._h, 3, 3, probs, 0, "block", 64, None,
+                                     s.cuda_stream) == _lib.GEMM_ERR_INVALID_ARG
+    assert _lib.gemm_run_grouped_fp8(h._h, 0, 3, probs, 0, "block", 1, None,
+                                     s.cuda_stream) == _lib.GEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    h.close()
