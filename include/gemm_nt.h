@@ -17,12 +17,21 @@
  * (any order the tiling chooses), but for given arguments every call on the
  * same device returns the same bits.
  *
- * Ownership: A, B and C are device pointers owned by the caller.  The handle
- * owns its workspace (FP32 split-K partial sums).
+ * The other entry points widen this product: gemm_run_ex adds a fused
+ * epilogue (scale, prior C, bias, activation), gemm_run_layout lets either
+ * operand be stored MN-major, gemm_run_fp8 takes FP8 operands with per-tensor
+ * or blockwise scales, and gemm_run_grouped / gemm_run_grouped_fp8 run a list
+ * of such products in one launch.
  *
- * Streams: gemm_run only enqueues work on `stream` (0 = the null stream) and
- * never synchronises.  One handle must not be used by two calls that may run
- * concurrently (its workspace is shared); use one handle per stream.
+ * Ownership: A, B and C are device pointers owned by the caller.  The handle
+ * owns its workspace (FP32 split-K partial sums, or a grouped launch's problem
+ * list) and a pinned staging buffer for grouped problem lists.
+ *
+ * Streams: every run call only enqueues work on `stream` (0 = the null stream)
+ * and never synchronises (a grouped call waits only for the copy out of its
+ * staging buffer made by the previous grouped call).  One handle must not be
+ * used by two calls that may run concurrently (its workspace is shared); use
+ * one handle per stream.
  *
  * Errors: every argument error is returned before any device work is enqueued.
  */
