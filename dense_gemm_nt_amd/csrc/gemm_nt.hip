@@ -14,6 +14,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <new>
 #include <vector>
@@ -122,10 +123,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         // panel of B), and split-K below to bring the grid up to the machine.
         cfg = CFG_PP2_256x256;
     } else {
-        // The 256x256 ping-pong tile when it fills at least half the machine on
-        // its own; smaller tiles otherwise.
-        const int64_t big = cdiv(M, 256) * cdiv(N, 256);
-        cfg = big >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_W4_128x128;
+        // The 256x256 ping-pong tile when its blocks fill at least half the
+        // machine, with the K splits the split rule below would give it (at
+        // least 20 k-slabs each); smaller tiles otherwise.
+        const int64_t big = std::max<int64_t>(1, cdiv(M, 256) * cdiv(N, 256));
+        const int64_t ksplit = std::min<int64_t>(kNumCUs / big, cdiv(K, 64) / 20);
+        cfg = big * std::max<int64_t>(1, ksplit) >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_W4_128x128;
     }
     if ((K % 8) && !kConfigs[cfg].kmask)
         cfg = CFG_W4_128x128_KMASK;
@@ -404,6 +407,8 @@ gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn f
     a.vec_store = (ldc % 4 == 0) && ((uintptr_t)C % vec_bytes == 0);
     const int64_t out_size = out_dtype == GEMM_FP32 ? 4 : 2;
     a.rows16 = ((ldc * out_size) % 16 == 0) && ((uintptr_t)C % 16 == 0);
+    // B, when at most two tile rows of blocks read it, is streamed
+    a.nt_b = p.tiles_m <= 2;
     a.partials = h->partials;
     a.alpha = 1.0f;
     if (epi) {
@@ -590,7 +595,8 @@ gemm_status_t run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
         const uintptr_t vec_bytes = out_dtype == GEMM_FP32 ? 16 : 8;
         d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
                   (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
-                  (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0);
+                  (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0) |
+                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0);
         descs.push_back(d);
         tiles += (int64_t)d.tiles_m * d.tiles_n;
         if (tiles >= INT32_MAX)
@@ -671,7 +677,8 @@ gemm_status_t run_grouped_fp8(gemm_handle_t h, int a_dtype, int b_dtype,
         const uintptr_t vec_bytes = out_dtype == GEMM_FP32 ? 16 : 8;
         d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
                   (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
-                  (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0);
+                  (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0) |
+                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0);
         descs.push_back(d);
         tiles += (int64_t)d.tiles_m * d.tiles_n;
         if (tiles >= INT32_MAX)

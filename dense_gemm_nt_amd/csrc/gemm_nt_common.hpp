@@ -34,13 +34,13 @@ struct GroupDesc {
     int lda, ldb, ldc;     // elements
     int tile_start;        // the group's first position in the launch's tile list
     int tiles_m, tiles_n, k_tiles;
-    int flags;             // GD_VEC_STORE | GD_ROWS16 | GD_BIAS_VEC
+    int flags;             // GD_VEC_STORE | GD_ROWS16 | GD_BIAS_VEC | GD_NT_B
     int sf_ld;             // FP8: k-blocks per scale row
     const float *scale_a;  // FP8: this group's scales (per tensor or blockwise)
     const float *scale_b;
     uint32_t sfa_bytes, sfb_bytes;
 };
-enum : int { GD_VEC_STORE = 1, GD_ROWS16 = 2, GD_BIAS_VEC = 4 };
+enum : int { GD_VEC_STORE = 1, GD_ROWS16 = 2, GD_BIAS_VEC = 4, GD_NT_B = 8 };
 
 struct KernelArgs {
     const uint16_t *A;
@@ -55,6 +55,8 @@ struct KernelArgs {
     int group_m;           // tile rows per group of the tile order
     int vec_store;         // 1 when 4 consecutive C elements may be stored as one vector
     int rows16;            // 1 when every row of C starts 16-byte aligned
+    int nt_b;              // 1: B is loaded with the non-temporal policy (at most two
+                           // tile rows, so each B element is read by at most two blocks)
     float *partials;       // split-K partials, dense [splits][M][N] FP32
     // fused epilogue D = act(alpha * acc + beta * C_old + bias), applied when epi != 0
     float alpha, beta;
@@ -95,6 +97,22 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t v
     asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
                  : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr));
+}
+
+// load_lds16 with the non-temporal cache policy when NT: for an operand whose
+// bytes the launch reads once or twice, so that its lines do not take the place
+// of lines many blocks will read again.  A template flag, so the policy is an
+// immediate of the instruction and the load path has no branch.
+template <bool NT>
+__device__ __forceinline__ void load_lds16_policy(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                                  uint32_t lds_addr)
+{
+    if constexpr (NT)
+        asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                     :
+                     : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr));
+    else
+        load_lds16(rs, voff, soff, lds_addr);
 }
 
 // One wave-wide 4-byte-per-lane load into LDS at lds_addr + 4 * lane (lanes
@@ -380,7 +398,9 @@ __device__ __forceinline__ void store_result(const KernelArgs &p, int split, int
 // off a single bank group.  Only the calling wave touches `stage`.
 // acc is [FN = 4][FM = 2] blocks of 32 x 32; the block's first element is
 // C[m0][n0] with m0, n0 relative to `dst`, which holds rows of `ld` elements.
-template <typename T>
+// NT stores with the non-temporal policy: for C, which the launch does not
+// read again (split-K partials, read next by the reduction, keep the default).
+template <typename T, bool NT = false>
 __device__ __forceinline__ void store_block_staged(const f32x16 (&acc)[4][2], uint8_t *stage, T *dst,
                                                    int64_t ld, int lane)
 {
@@ -433,7 +453,10 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&acc)[4][2], ui
             const int c = lane % LPR;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * ROWB + ((c ^ (r & 15)) * 16));
             T *g = dst + (int64_t)(pass * ROWS + r) * ld + c * (16 / ES);
-            *reinterpret_cast<u32x4 *>(g) = v;
+            if constexpr (NT)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(g));
+            else
+                *reinterpret_cast<u32x4 *>(g) = v;
         }
         wait_lgkmcnt0();
     }

@@ -38,6 +38,8 @@
 //    atomics, no inter-workgroup waiting.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_nt_common.hpp"
 
 namespace gnt {
@@ -98,21 +100,29 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
     const uint32_t ldsA = lds_base;
     const uint32_t ldsB = lds_base + STAGES * A_BYTES;
 
+    // One stage's loads; B's take the non-temporal policy when B is streamed
+    // (one branch per stage picks the copy with that policy).
     auto issue = [&](int kt, int s) {
         const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * 2);
         const bool kin = lc * 8 < p.K - kt * BK;
+        auto loads = [&](auto nt) {
 #pragma unroll
-        for (int j = 0; j < A_LOADS; ++j) {
-            const uint32_t v = (kin && lrow0 + j * RSTEP < rows_a) ? voffA : kOutOfRange;
-            load_lds16(rsA, v, koff + (uint32_t)(j * RSTEP) * lda2,
-                       ldsA + s * A_BYTES + (j * NWAVES + wave) * 1024);
-        }
+            for (int j = 0; j < A_LOADS; ++j) {
+                const uint32_t v = (kin && lrow0 + j * RSTEP < rows_a) ? voffA : kOutOfRange;
+                load_lds16(rsA, v, koff + (uint32_t)(j * RSTEP) * lda2,
+                           ldsA + s * A_BYTES + (j * NWAVES + wave) * 1024);
+            }
 #pragma unroll
-        for (int j = 0; j < B_LOADS; ++j) {
-            const uint32_t v = (kin && lrow0 + j * RSTEP < rows_b) ? voffB : kOutOfRange;
-            load_lds16(rsB, v, koff + (uint32_t)(j * RSTEP) * ldb2,
-                       ldsB + s * B_BYTES + (j * NWAVES + wave) * 1024);
-        }
+            for (int j = 0; j < B_LOADS; ++j) {
+                const uint32_t v = (kin && lrow0 + j * RSTEP < rows_b) ? voffB : kOutOfRange;
+                load_lds16_policy<decltype(nt)::value>(rsB, v, koff + (uint32_t)(j * RSTEP) * ldb2,
+                                                       ldsB + s * B_BYTES + (j * NWAVES + wave) * 1024);
+            }
+        };
+        if (p.nt_b)
+            loads(std::true_type{});
+        else
+            loads(std::false_type{});
     };
 
     // Per-lane LDS read offsets of the MFMA operand chunk for each k16 step.

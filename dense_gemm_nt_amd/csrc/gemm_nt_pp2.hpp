@@ -148,9 +148,10 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // per-slab buffer resource ends with k-row K - 1, so k-rows past K read
         // zeros.
         const int mn_chunk = (lane & 15) ^ (4 * (lane >> 4));
-        auto load_one = [&](auto is_a, int i, int row0, int u, int j) {
+        auto load_one = [&](auto is_a, int i, int row0, int u, int j, auto nt) {
             constexpr bool IS_A = decltype(is_a)::value;
             constexpr bool MN = IS_A ? AM : BNM;
+            constexpr bool NT = decltype(nt)::value;
             const int kt = kt0 + i;
             const uint32_t dst = lds0 + (uint32_t)(u * UNIT + (j * 4 + q) * 1024);
             if constexpr (MN) {
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                 const uint32_t v = col < (IS_A ? rows_a : rows_b)
                                        ? (uint32_t)(4 * q + (lane >> 4)) * ld2 + (uint32_t)col * 2u
                                        : kOutOfRange;
-                load_lds16(rs, v, (uint32_t)(16 * j) * ld2, dst);
+                load_lds16_policy<NT>(rs, v, (uint32_t)(16 * j) * ld2, dst);
             } else {
                 const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * ESZ);
                 const bool kin = lc * 16 < (p.K - kt * BK) * ESZ;
@@ -178,18 +179,19 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                 const int rows = IS_A ? rows_a : rows_b;
                 const uint32_t ld2 = IS_A ? lda2 : ldb2;
                 const uint32_t v = (kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange;
-                load_lds16(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2, dst);
+                load_lds16_policy<NT>(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2, dst);
             }
         };
         // The eight loads a wave issues in one memory phase, n = 0..7: group 0
         // loads both halves of B(i) into B slot i % 2 (GRP = 0), group 1 both
         // halves of A(i) (GRP = 1).
-        auto group_load = [&](auto grp, int i, int n) {
+        auto group_load = [&](auto grp, int i, int n, auto nt) {
             const int j = n & 3, half = n >> 2;
             if constexpr (decltype(grp)::value == 0)
-                load_one(std::false_type{}, i, half * 128, U_B + 2 * (i & 1) + half, j);
+                load_one(std::false_type{}, i, half * 128, U_B + 2 * (i & 1) + half, j, nt);
             else
-                load_one(std::true_type{}, i, half * 128, half == 0 ? U_A0 + (i & 1) : U_A1 + (i % 3), j);
+                load_one(std::true_type{}, i, half * 128, half == 0 ? U_A0 + (i & 1) : U_A1 + (i % 3), j,
+                         std::false_type{});
         };
 
         // Blockwise scales of local slab i (SC == 1).  Group 1 wave q loads the
@@ -304,13 +306,24 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
         // fragment reads of slab i.  Loads first: their issue is what the vector
         // memory unit paces, and the reads overlap it.
-        auto memory_phase = [&](auto grp, int i, bool has_load, int li) {
-            if (has_load) {
+        // The 8 loads of slab `li` and its scales.  Group 0's B loads take the
+        // non-temporal policy when B is streamed: one branch per phase picks the
+        // copy of the eight loads with that policy.
+        auto issue_loads = [&](auto grp, int li) {
+            auto eight = [&](auto nt) {
     #pragma unroll
                 for (int n = 0; n < 8; ++n)
-                    group_load(grp, li, n);
+                    group_load(grp, li, n, nt);
                 scale_load(grp, li);
-            }
+            };
+            if (decltype(grp)::value == 0 && p.nt_b)
+                eight(std::true_type{});
+            else
+                eight(std::false_type{});
+        };
+        auto memory_phase = [&](auto grp, int i, bool has_load, int li) {
+            if (has_load)
+                issue_loads(grp, li);
     #pragma unroll
             for (int r = 0; r < 24; ++r)
                 read_one(grp, i, r);
@@ -387,21 +400,12 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             // Prologue: B(0) by group 0; A(0), A(1) by group 1.  Slab 0 lands before
             // phase 0; A(1) by the end of phase 1 (the steady-state wait).
             if (group == 0) {
-    #pragma unroll
-                for (int n = 0; n < 8; ++n)
-                    group_load(G0{}, 0, n);
-                scale_load(G0{}, 0);
+                issue_loads(G0{}, 0);
                 wait_vmcnt<0>();
             } else {
-    #pragma unroll
-                for (int n = 0; n < 8; ++n)
-                    group_load(G1{}, 0, n);
-                scale_load(G1{}, 0);
+                issue_loads(G1{}, 0);
                 if (nk > 1) {
-    #pragma unroll
-                    for (int n = 0; n < 8; ++n)
-                        group_load(G1{}, 1, n);
-                    scale_load(G1{}, 1);
+                    issue_loads(G1{}, 1);
                     wait_vmcnt<A_INFLIGHT>();
                 } else {
                     wait_vmcnt<0>();
@@ -478,11 +482,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         }
         if (full && p.splits == 1 && p.rows16) {
             if constexpr (OUT == OUT_BF16)
-                store_block_staged<__bf16>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+                store_block_staged<__bf16, true>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
             else if constexpr (OUT == OUT_FP16)
-                store_block_staged<_Float16>(acc, stage, static_cast<_Float16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+                store_block_staged<_Float16, true>(acc, stage, static_cast<_Float16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
             else
-                store_block_staged<float>(acc, stage, static_cast<float *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+                store_block_staged<float, true>(acc, stage, static_cast<float *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
             return;
         }
     #pragma unroll
@@ -532,6 +536,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         p.vec_store = flags & GD_VEC_STORE ? 1 : 0;
         p.rows16 = flags & GD_ROWS16 ? 1 : 0;
         p.bias_vec = flags & GD_BIAS_VEC ? 1 : 0;
+        p.nt_b = flags & GD_NT_B ? 1 : 0;
         if constexpr (F8) {
             p.scale_a = static_cast<const float *>(uptr(d->scale_a));
             p.scale_b = static_cast<const float *>(uptr(d->scale_b));
