@@ -306,24 +306,17 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
         // fragment reads of slab i.  Loads first: their issue is what the vector
         // memory unit paces, and the reads overlap it.
-        // The 8 loads of slab `li` and its scales.  Group 0's B loads take the
-        // non-temporal policy when B is streamed: one branch per phase picks the
-        // copy of the eight loads with that policy.
-        auto issue_loads = [&](auto grp, int li) {
-            auto eight = [&](auto nt) {
+        // The 8 loads of slab `li` and its scales; `nt` (a compile-time flag)
+        // gives group 0's B loads the non-temporal policy.
+        auto issue_loads = [&](auto grp, int li, auto nt) {
     #pragma unroll
-                for (int n = 0; n < 8; ++n)
-                    group_load(grp, li, n, nt);
-                scale_load(grp, li);
-            };
-            if (decltype(grp)::value == 0 && p.nt_b)
-                eight(std::true_type{});
-            else
-                eight(std::false_type{});
+            for (int n = 0; n < 8; ++n)
+                group_load(grp, li, n, nt);
+            scale_load(grp, li);
         };
-        auto memory_phase = [&](auto grp, int i, bool has_load, int li) {
+        auto memory_phase = [&](auto grp, int i, bool has_load, int li, auto nt) {
             if (has_load)
-                issue_loads(grp, li);
+                issue_loads(grp, li, nt);
     #pragma unroll
             for (int r = 0; r < 24; ++r)
                 read_one(grp, i, r);
@@ -400,12 +393,15 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             // Prologue: B(0) by group 0; A(0), A(1) by group 1.  Slab 0 lands before
             // phase 0; A(1) by the end of phase 1 (the steady-state wait).
             if (group == 0) {
-                issue_loads(G0{}, 0);
+                if (SC != 1 && p.nt_b)
+                    issue_loads(G0{}, 0, std::integral_constant<bool, SC != 1>{});
+                else
+                    issue_loads(G0{}, 0, std::false_type{});
                 wait_vmcnt<0>();
             } else {
-                issue_loads(G1{}, 0);
+                issue_loads(G1{}, 0, std::false_type{});
                 if (nk > 1) {
-                    issue_loads(G1{}, 1);
+                    issue_loads(G1{}, 1, std::false_type{});
                     wait_vmcnt<A_INFLIGHT>();
                 } else {
                     wait_vmcnt<0>();
@@ -413,20 +409,29 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             }
             phase_end();
             if (group == 0) {
-                for (int i = 0; i < nk; ++i) {
-                    GNT_PP2_EVENT(i, 0);
-                    memory_phase(G0{}, i, i + 1 < nk, i + 1);        // B(i+1)
-                    wait_lgkmcnt0();
-                    GNT_PP2_EVENT(i, 1);
-                    phase_end();                               // end of phase 2i
-                    GNT_PP2_EVENT(i, 2);
-                    compute_slab();
-                    __builtin_amdgcn_sched_barrier(0);
-                    GNT_PP2_EVENT(i, 3);
-                    wait_vmcnt<0>();                           // B(i+1) landed
-                    GNT_PP2_EVENT(i, 4);
-                    phase_end();                               // end of phase 2i+1
-                }
+                // two copies of the loop, for the two policies of the B loads
+                auto g0_loop = [&](auto nt) {
+                    for (int i = 0; i < nk; ++i) {
+                        GNT_PP2_EVENT(i, 0);
+                        memory_phase(G0{}, i, i + 1 < nk, i + 1, nt);    // B(i+1)
+                        wait_lgkmcnt0();
+                        GNT_PP2_EVENT(i, 1);
+                        phase_end();                               // end of phase 2i
+                        GNT_PP2_EVENT(i, 2);
+                        compute_slab();
+                        __builtin_amdgcn_sched_barrier(0);
+                        GNT_PP2_EVENT(i, 3);
+                        wait_vmcnt<0>();                           // B(i+1) landed
+                        GNT_PP2_EVENT(i, 4);
+                        phase_end();                               // end of phase 2i+1
+                    }
+                };
+                // (blockwise FP8 keeps one copy, with the default policy: a second
+                // one does not fit its registers)
+                if (SC != 1 && p.nt_b)
+                    g0_loop(std::integral_constant<bool, SC != 1>{});
+                else
+                    g0_loop(std::false_type{});
             } else {
                 for (int i = 0; i < nk; ++i) {
                     GNT_PP2_EVENT(i, 0);
@@ -436,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     GNT_PP2_EVENT(i, 1);
                     phase_end();                               // end of phase 2i
                     GNT_PP2_EVENT(i, 2);
-                    memory_phase(G1{}, i, i + 2 < nk, i + 2);        // A(i+2)
+                    memory_phase(G1{}, i, i + 2 < nk, i + 2, std::false_type{});   // A(i+2)
                     wait_lgkmcnt0();
                     GNT_PP2_EVENT(i, 3);
                     if (i + 2 < nk)                            // A(i+1) landed
