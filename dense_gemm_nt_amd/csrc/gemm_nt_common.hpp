@@ -386,6 +386,55 @@ __device__ __forceinline__ void store_result(const KernelArgs &p, int split, int
     }
 }
 
+// One wave's block of C (or of a split-K partial) written through LDS with
+// lane-contiguous stores, for any row alignment of the output.  The block is
+// (32 FM) x (32 FN) accumulators in the MFMA layout: lane l holds rows
+// 32 fm + l % 32, columns 32 fn + 8 q + 4 (l / 32) .. +4.  It is staged as FP32
+// rows of 32 FN values, the 16-byte chunk c of row r at chunk c ^ (r & KEYM), so
+// the column-wise staging writes spread over the banks.  The read-back gives
+// lane l consecutive columns of one row, so every store instruction (4 or 2
+// bytes per lane) writes whole row segments, where the direct stores of the
+// MFMA layout touch 32 rows per instruction.  Elements at or past (rows, cols)
+// are not stored.  Only the calling wave touches `stage`
+// (4096 FM FN bytes).
+template <int OUT, int FN, int FM>
+__device__ __forceinline__ void store_block_rows(const f32x16 (&acc)[FN][FM], uint8_t *stage, void *C,
+                                                 int64_t ld, int rows, int cols, int lane)
+{
+    constexpr int DPR = 32 * FN;                      // values per staged row
+    constexpr int ROWB = 4 * DPR;
+    constexpr int KEYM = (DPR / 4 < 16 ? DPR / 4 : 16) - 1;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = fm * 32 + (lane & 31);
+                const int c = fn * 8 + 2 * q + (lane >> 5);
+                const f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                 acc[fn][fm][4 * q + 3]};
+                *reinterpret_cast<f32x4 *>(stage + r * ROWB + ((c ^ (r & KEYM)) * 16)) = v;
+            }
+    wait_lgkmcnt0();
+#pragma unroll 4
+    for (int i = 0; i < FM * FN * 16; ++i) {
+        const int idx = i * 64 + lane;
+        const int r = idx / DPR, c = idx % DPR;
+        const float x = *reinterpret_cast<const float *>(stage + r * ROWB + (((c >> 2) ^ (r & KEYM)) * 16) +
+                                                         (c & 3) * 4);
+        if (r < rows && c < cols) {
+            const int64_t off = (int64_t)r * ld + c;
+            if constexpr (OUT == OUT_FP32)
+                static_cast<float *>(C)[off] = x;
+            else if constexpr (OUT == OUT_BF16)
+                static_cast<uint16_t *>(C)[off] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+            else
+                static_cast<uint16_t *>(C)[off] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+        }
+    }
+}
+
 // Epilogue through LDS for one wave's 64 x 128 block of C (full tile only).
 // Staging C through shared memory and storing it with wide row-contiguous
 // writes is what "Optimizing GEMMs using tcgen05 - Part 1" measures as its last

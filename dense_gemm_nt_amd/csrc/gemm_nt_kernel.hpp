@@ -214,6 +214,29 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
         }
     }
 
+    // Epilogue without a fused epilogue: each wave's block through its share of
+    // the (now idle) LDS ring, stored row-contiguously (C, or this split's
+    // FP32 partial).  A block-uniform branch, so the barrier that retires the
+    // ring's last fragment reads is reached by every wave.
+    constexpr int STAGE_BYTES = 4096 * FM * FN;
+    if constexpr (NWAVES * STAGE_BYTES <= STAGES * (A_BYTES + B_BYTES)) {
+        if (!p.epi) {
+            const int r0 = m0 + wave_m * WTM, c0 = n0 + wave_n * WTN;
+            wg_barrier();
+            uint8_t *stage = smem + wave * STAGE_BYTES;
+            if (p.splits > 1)
+                store_block_rows<OUT_FP32>(acc, stage, p.partials + (int64_t)split * p.M * p.N + (int64_t)r0 * p.N + c0,
+                                           p.N, p.M - r0, p.N - c0, lane);
+            else if constexpr (OUT == OUT_FP32)
+                store_block_rows<OUT>(acc, stage, static_cast<float *>(p.C) + (int64_t)r0 * p.ldc + c0, p.ldc,
+                                      p.M - r0, p.N - c0, lane);
+            else
+                store_block_rows<OUT>(acc, stage, static_cast<uint16_t *>(p.C) + (int64_t)r0 * p.ldc + c0, p.ldc,
+                                      p.M - r0, p.N - c0, lane);
+            return;
+        }
+    }
+
     // Epilogue: convert and store.  Lane holds C[m][n .. n+3] per 4-register group.
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
