@@ -70,6 +70,7 @@ const Config kConfigs[] = {
     {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 131072, 1, 1, gnt::kTile128x128_w4_s4_kmask},
     {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 131072, 0, 1, gnt::kPingpong256},
     {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk},
+    {"128x128x64_w4_s2", 128, 128, 64, 4, 2, 65536, 0, 1, gnt::kTile128x128_w4_s2},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
@@ -80,6 +81,7 @@ enum {
     CFG_W4_128x128_KMASK = 4,
     CFG_PP_256x256 = 5,
     CFG_PP2_256x256 = 6,
+    CFG_W4_128x128_S2 = 7,
 };
 
 struct Plan {
@@ -129,6 +131,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         const int64_t big = std::max<int64_t>(1, cdiv(M, 256) * cdiv(N, 256));
         const int64_t ksplit = std::min<int64_t>(kNumCUs / big, cdiv(K, 64) / 20);
         cfg = big * std::max<int64_t>(1, ksplit) >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_W4_128x128;
+    }
+    // 128x128 tiles that overflow one pass of the machine but fit two: the
+    // two-stage ring (64 KB of LDS) lets two blocks share a compute unit, so
+    // they all run at once instead of leaving a second, nearly empty wave.
+    if (cfg == CFG_W4_128x128 && force_cfg < 0) {
+        const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
+        if (t128 > kNumCUs && t128 <= 2 * kNumCUs)
+            cfg = CFG_W4_128x128_S2;
     }
     if ((K % 8) && !kConfigs[cfg].kmask)
         cfg = CFG_W4_128x128_KMASK;

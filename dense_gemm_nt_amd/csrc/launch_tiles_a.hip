@@ -27,6 +27,7 @@ LaunchTable kTile128x128_w4_s4 = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, false);
 #else
 LaunchTable kTile32x256_w4_s4 = GNT_TILE_TABLE(32, 256, 64, 1, 4, 4, false);
 LaunchTable kTile128x128_w4_s4_kmask = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, true);
+LaunchTable kTile128x128_w4_s2 = GNT_TILE_TABLE(128, 128, 64, 2, 2, 2, false);
 #endif
 
 }  // namespace gnt

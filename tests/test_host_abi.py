@@ -130,8 +130,10 @@ def test_plan_regimes(g):
     # mid-size M with a long K: the 256x256 tile with K splits fills the machine
     p = g.gemm_plan(512, 8192, 8192)
     assert p["name"] == "256x256x64_w8_pp2" and p["splits"] > 1 and p["workgroups"] >= 128
-    # ... and with a short K the smaller tile keeps the compute units busy
-    assert g.gemm_plan(1000, 4097, 1536)["name"] == "128x128x64_w4_s4"
+    # ... and with a short K the smaller tile keeps the compute units busy: two
+    # blocks per compute unit when its tiles overflow one pass of the machine
+    assert g.gemm_plan(1000, 4097, 1536)["name"] == "128x128x64_w4_s2"
+    assert g.gemm_plan(1000, 4096, 1536)["name"] == "128x128x64_w4_s4"
 
 
 def test_run_layout_rejects_null_handle_before_any_device_work(g):
