@@ -303,9 +303,6 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                                                                       roff(ks));
             }
         };
-        // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
-        // fragment reads of slab i.  Loads first: their issue is what the vector
-        // memory unit paces, and the reads overlap it.
         // The 8 loads of slab `li` and its scales; `nt` (a compile-time flag)
         // gives group 0's B loads the non-temporal policy.
         auto issue_loads = [&](auto grp, int li, auto nt) {
@@ -314,6 +311,9 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                 group_load(grp, li, n, nt);
             scale_load(grp, li);
         };
+        // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
+        // fragment reads of slab i.  Loads first: their issue is what the vector
+        // memory unit paces, and the reads overlap it.
         auto memory_phase = [&](auto grp, int i, bool has_load, int li, auto nt) {
             if (has_load)
                 issue_loads(grp, li, nt);
