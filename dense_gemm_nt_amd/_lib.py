@@ -35,7 +35,8 @@ class GemmPlan(ctypes.Structure):
                 ("waves", ctypes.c_int), ("stages", ctypes.c_int), ("splits", ctypes.c_int),
                 ("lds_bytes", ctypes.c_int),
                 ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_int64), ("name", ctypes.c_char * 48)]
+                ("workspace_bytes", ctypes.c_int64), ("name", ctypes.c_char * 48),
+                ("streamk", ctypes.c_int)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}

@@ -49,6 +49,19 @@ hipError_t launch_splitk_sum(const KernelArgs &a, int out_dtype, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_streamk_sum(const KernelArgs &a, int G, int out_dtype, hipStream_t s)
+{
+    const int64_t threads = (int64_t)a.M * ((a.N + 3) / 4);
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    if (out_dtype == GEMM_BF16)
+        hipLaunchKernelGGL(gnt::streamk_sum<gnt::OUT_BF16>, dim3(grid), dim3(256), 0, s, a, G);
+    else if (out_dtype == GEMM_FP16)
+        hipLaunchKernelGGL(gnt::streamk_sum<gnt::OUT_FP16>, dim3(grid), dim3(256), 0, s, a, G);
+    else
+        hipLaunchKernelGGL(gnt::streamk_sum<gnt::OUT_FP32>, dim3(grid), dim3(256), 0, s, a, G);
+    return hipGetLastError();
+}
+
 struct Config {
     const char *name;
     int bm, bn, bk, waves, stages;
@@ -86,6 +99,9 @@ enum {
 
 struct Plan {
     int cfg;
+    int stream;            // stream-K: the persistent ping-pong kernel + streamk_sum
+    int sk_maxseg;         // stream-K partial slots per block
+    int64_t sk_units;      // stream-K units, tiles * k_tiles
     int tiles_m, tiles_n;
     int k_tiles;
     int splits;
@@ -107,7 +123,8 @@ int find_config(const char *name)
 
 // Pick the tile shape and the K split for a problem.  `ws_bytes` bounds the
 // split-K partial storage; `force_cfg` / `force_splits` (>= 0 / > 0) override.
-Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg, int force_splits)
+Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg, int force_splits,
+               int streamk = 0)
 {
     Plan p{};
     int cfg;
@@ -180,6 +197,32 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         p.group_m = 1;
     p.grid = tiles * splits;
     p.ws_bytes = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+
+    // Stream-K (the CuTe page's section 9 names it beside split-K): when the
+    // ping-pong tiles with their K splits leave at least 3/8 of the compute
+    // units idle, every unit takes an equal run of the tiles * k_tiles
+    // (tile, k-slab) units instead, each tile it touches giving one partial
+    // (a 256 KB slot).  Only for runs of at least 32 k-slabs: each segment
+    // refills the pipeline and writes a whole partial tile, which shorter runs
+    // do not pay back.  `streamk`: 0 never (callers without the persistent
+    // ping-pong kernel), 1 by this rule, 2 whenever the tile is the ping-pong one.
+    if (streamk > 0 && cfg == CFG_PP2_256x256 && force_splits <= 0 && tiles > 0 && p.k_tiles > 0) {
+        const int64_t T = tiles * p.k_tiles;
+        const int64_t G = std::min<int64_t>(kNumCUs, T);
+        const int64_t L = (T + G - 1) / G;                 // longest run
+        const int maxseg = (int)((L - 1) / p.k_tiles + 2);
+        const int64_t ws = G * maxseg * (int64_t)256 * 256 * 4;
+        const bool idle = p.grid * 8 <= (int64_t)kNumCUs * 5;
+        if (ws <= ws_bytes && T < INT32_MAX && (streamk == 2 || (idle && L >= 32))) {
+            p.stream = 1;
+            p.sk_units = T;
+            p.sk_maxseg = maxseg;
+            p.splits = 1;
+            p.kt_per_split = p.k_tiles;
+            p.grid = G;
+            p.ws_bytes = ws;
+        }
+    }
     return p;
 }
 
@@ -192,6 +235,8 @@ struct gemm_handle_s {
     int force_cfg;
     int force_splits;
     int persistent;    // GEMM_PERSIST=1: ping-pong tiles run by 256 persistent blocks
+    int streamk;       // GEMM_STREAMK: 0 off, 1 by the plan rule (default), 2 whenever
+                       // the ping-pong tile is planned
     int log;
     // grouped launches: pinned staging of the problem list and an event that
     // marks when the last copy out of it has run
@@ -269,7 +314,7 @@ gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
         return GEMM_ERR_INVALID_ARG;
     if (M >= INT32_MAX || N >= INT32_MAX || K >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
-    const Plan p = make_plan(M, N, K, kDefaultWorkspaceMB << 20, -1, -1);
+    const Plan p = make_plan(M, N, K, kDefaultWorkspaceMB << 20, -1, -1, 1);
     const Config &c = kConfigs[p.cfg];
     out->block_m = c.bm;
     out->block_n = c.bn;
@@ -281,6 +326,7 @@ gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
     out->tiles = (int64_t)p.tiles_m * p.tiles_n;
     out->workgroups = (M == 0 || N == 0) ? 0 : p.grid;
     out->workspace_bytes = p.ws_bytes;
+    out->streamk = p.stream;
     snprintf(out->name, sizeof(out->name), "%s", c.name);
     return GEMM_OK;
 }
@@ -310,6 +356,9 @@ gemm_status_t gemm_create(gemm_handle_t *out)
         h->force_splits = atoi(e);
     if (const char *e = getenv("GEMM_PERSIST"))
         h->persistent = atoi(e) != 0;
+    h->streamk = 1;
+    if (const char *e = getenv("GEMM_STREAMK"))
+        h->streamk = atoi(e);
     if (const char *e = getenv("GEMM_LOG"))
         h->log = atoi(e);
     h->ws_bytes = mb << 20;
@@ -398,7 +447,7 @@ gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn f
                       int64_t M, int64_t N, int64_t K, int64_t ldc, int out_dtype,
                       const gemm_epilogue_t *epi, hipStream_t stream)
 {
-    if (p.splits > 1 && p.ws_bytes > h->ws_bytes)
+    if ((p.splits > 1 || p.stream) && p.ws_bytes > h->ws_bytes)
         return GEMM_ERR_UNSUPPORTED;
     if (p.grid <= 0 || p.grid >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
@@ -420,6 +469,8 @@ gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn f
     // B, when at most two tile rows of blocks read it, is streamed
     a.nt_b = p.tiles_m <= 2;
     a.partials = h->partials;
+    a.sk_units = p.stream ? (int)p.sk_units : 0;
+    a.sk_maxseg = p.sk_maxseg;
     a.alpha = 1.0f;
     if (epi) {
         a.alpha = epi->alpha;
@@ -432,12 +483,14 @@ gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn f
                   a.act == GEMM_ACT_NONE);
     }
     if (h->log)
-        fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld\n",
+        fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld%s\n",
                 (long long)M, (long long)N, (long long)K, kConfigs[p.cfg].name, p.tiles_m,
-                p.tiles_n, p.splits, p.kt_per_split, (long long)p.grid);
+                p.tiles_n, p.splits, p.kt_per_split, (long long)p.grid, p.stream ? " stream-K" : "");
     hipError_t e = fn(a, (unsigned)p.grid, stream);
     if (e == hipSuccess && p.splits > 1)
         e = launch_splitk_sum(a, out_dtype, stream);
+    if (e == hipSuccess && p.stream)
+        e = launch_streamk_sum(a, (int)p.grid, out_dtype, stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
@@ -473,7 +526,7 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     if (!nt && h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
         return GEMM_ERR_UNSUPPORTED;
     const Plan p = make_plan(M, N, K, h->ws_bytes, nt ? h->force_cfg : CFG_PP2_256x256,
-                             h->force_splits);
+                             h->force_splits, nt ? h->streamk : 0);
     KernelArgs a{};
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);
@@ -482,7 +535,9 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     launch_fn fn = nt ? kConfigs[p.cfg].fn[in_dtype][out_dtype]
                       : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
     Plan q = p;
-    if (nt && h->persistent && p.cfg == CFG_PP2_256x256 && p.grid > kNumCUs) {
+    if (p.stream) {
+        fn = gnt::kPP2_persistent[in_dtype][out_dtype];   // its stream-K mode
+    } else if (nt && h->persistent && p.cfg == CFG_PP2_256x256 && p.grid > kNumCUs) {
         fn = gnt::kPP2_persistent[in_dtype][out_dtype];
         q.grid = kNumCUs;
     }

@@ -57,7 +57,11 @@ struct KernelArgs {
     int rows16;            // 1 when every row of C starts 16-byte aligned
     int nt_b;              // 1: B is loaded with the non-temporal policy (at most two
                            // tile rows, so each B element is read by at most two blocks)
-    float *partials;       // split-K partials, dense [splits][M][N] FP32
+    float *partials;       // split-K partials, dense [splits][M][N] FP32; stream-K
+                           // partials, [block][segment][256][256] FP32
+    int sk_units;          // stream-K: tiles * k_tiles (0: off); block b of the grid G
+                           // takes units [b T / G, (b + 1) T / G) in tile-major order
+    int sk_maxseg;         // stream-K: partial slots per block
     // fused epilogue D = act(alpha * acc + beta * C_old + bias), applied when epi != 0
     float alpha, beta;
     const float *bias;     // FP32, N values (bias_along == 1) or M values (2)
@@ -658,6 +662,39 @@ __global__ __launch_bounds__(256) void splitk_sum(KernelArgs p)
             for (int i = 0; i < 4; ++i)
                 if (i < valid)
                     sum[i] += src[s * plane + i];
+    }
+    if (p.epi)
+        sum = epilogue4<OUT>(p, m, n, sum, valid);
+    store4<OUT>(p.C, (int64_t)m * p.ldc + n, sum, p.vec_store != 0, valid);
+}
+
+// Stream-K reduction: the outputs of tile t are the sum of the partials of
+// the blocks whose unit ranges meet [t k_tiles, (t + 1) k_tiles), added in block
+// order (a fixed order, so results are reproducible), then the epilogue and the
+// store.  Block b's range starts at floor(b T / G); the block holding unit u is
+// ceil((u + 1) G / T) - 1, and tile t is segment t - floor(start(b) / k_tiles)
+// of block b.  One thread per group of four consecutive outputs of a row.
+template <int OUT>
+__global__ __launch_bounds__(256) void streamk_sum(KernelArgs p, int G)
+{
+    const int nvec = (p.N + 3) >> 2;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)p.M * nvec)
+        return;
+    const int m = (int)(t / nvec);
+    const int n = (int)(t - (int64_t)m * nvec) * 4;
+    const int valid = p.N - n;
+    const int tile = (m >> 8) * p.tiles_n + (n >> 8);
+    const int64_t T = p.sk_units;
+    const int64_t u0 = (int64_t)tile * p.k_tiles, u1 = u0 + p.k_tiles - 1;
+    const int b0 = (int)(((u0 + 1) * G + T - 1) / T - 1);
+    const int b1 = (int)(((u1 + 1) * G + T - 1) / T - 1);
+    const int in_tile = (m & 255) * 256 + (n & 255);
+    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = b0; b <= b1; ++b) {
+        const int seg = tile - (int)(((int64_t)b * T / G) / p.k_tiles);
+        const float *src = p.partials + ((int64_t)b * p.sk_maxseg + seg) * 65536 + in_tile;
+        sum += *reinterpret_cast<const f32x4 *>(src);
     }
     if (p.epi)
         sum = epilogue4<OUT>(p, m, n, sum, valid);

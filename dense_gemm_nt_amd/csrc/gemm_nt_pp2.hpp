@@ -102,9 +102,16 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
 
     KernelArgs p = p0;
 
+    const bool streamk = PS && p.sk_units > 0;
+
     // One output tile (split `split` of tile (tm, tn)): prologue, main loop and
-    // epilogue.  Run once per block, or in a loop by persistent blocks.
-    auto tile = [&](int tm, int tn, int split_) {
+    // epilogue.  Run once per block, or in a loop by persistent blocks.  A
+    // stream-K segment is k-slabs [sk_kt0, +sk_nk) of the tile, its FP32
+    // partial into slot sk_slot of the workspace.
+    // (Always inlined: called from two loops it would otherwise become a real
+    // call, which passes the captured arguments through memory.)
+    auto tile = [&](int tm, int tn, int split_, int sk_kt0 = 0, int sk_nk = 0,
+                    int sk_slot = 0) __attribute__((always_inline)) {
         // Persistent blocks: an opaque copy of the lane id, so the per-lane
         // offsets derived from it are recomputed per work unit instead of
         // being held across the epilogue.
@@ -113,8 +120,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             asm volatile("" : "+v"(lane));
         const int split = split_;
         const int m0 = tm * BM, n0 = tn * BN;
-        const int kt0 = split * p.kt_per_split;
-        const int nk = min(p.k_tiles, kt0 + p.kt_per_split) - kt0;
+        const int kt0 = streamk ? sk_kt0 : split * p.kt_per_split;
+        const int nk = streamk ? sk_nk : min(p.k_tiles, kt0 + p.kt_per_split) - kt0;
 
         const int rows_a = min(BM, p.M - m0);
         const int rows_b = min(BN, p.N - n0);
@@ -476,6 +483,12 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         }
         const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
         uint8_t *stage = smem + wave * 16384;
+        if (streamk) {
+            // a whole 256 x 256 slot per segment, ragged tiles included
+            float *ws = p.partials + (int64_t)sk_slot * (BM * BN);
+            store_block_staged<float>(acc, stage, ws + wm0 * BN + wn0, BN, lane);
+            return;
+        }
         if (full && p.splits > 1 && (p.N & 3) == 0) {
             float *ws = p.partials + (int64_t)split * p.M * p.N;
             store_block_staged<float>(acc, stage, ws + (int64_t)(m0 + wm0) * p.N + (n0 + wn0), p.N, lane);
@@ -553,6 +566,26 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         tile_order(v - u32(d->tile_start), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
         tile(tm, tn, split);
     } else if constexpr (PS) {
+        if (streamk) {
+            // Stream-K: block b takes the contiguous units [b T / G, (b + 1) T / G)
+            // of the T = tiles * k_tiles (tile, k-slab) units in tile-major order,
+            // one segment per tile it touches; a barrier between segments, as
+            // between the persistent loop's units below.
+            // (T < 2^31, checked by the host; the values are wave-uniform)
+            auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+            const int T = uni(p.sk_units), G = uni((int)gridDim.x);
+            int u = uni((int)((int64_t)blockIdx.x * T / G));
+            const int end = uni((int)((int64_t)(blockIdx.x + 1) * T / G));
+            for (int seg = 0; u < end; ++seg) {
+                const int t = uni(u / p.k_tiles);
+                const int e = min(end, (t + 1) * p.k_tiles);
+                tile(uni(t / p.tiles_n), uni(t % p.tiles_n), 0, uni(u - t * p.k_tiles), uni(e - u),
+                     uni((int)blockIdx.x * p.sk_maxseg + seg));
+                wg_barrier();
+                u = e;
+            }
+            return;
+        }
         // Persistent blocks (grid a multiple of 8, at most the work units):
         // XCD x (the blocks with id % 8 == x) owns the contiguous run
         // [x T / 8, (x + 1) T / 8) of the T work units in tile order, and its

@@ -253,8 +253,11 @@ typedef struct {
     int lds_bytes;                 /* LDS the kernel allocates per workgroup */
     int64_t tiles;                 /* output tiles */
     int64_t workgroups;            /* grid size */
-    int64_t workspace_bytes;       /* split-K partials used (splits * M * N * 4) */
+    int64_t workspace_bytes;       /* split-K partials used (splits * M * N * 4), or the
+                                      stream-K slots (workgroups * segments * 256 KB) */
     char name[48];                 /* kernel configuration name */
+    int streamk;                   /* 1: stream-K (each workgroup an equal run of the
+                                      tiles * k-slabs units, then a reduction kernel) */
 } gemm_plan_t;
 
 gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,

@@ -20,12 +20,17 @@ def say(msg):
     sys.stdout.flush()
 
 
-def new_handle(config=None, splits=None, persistent=False):
+def new_handle(config=None, splits=None, persistent=False, streamk=None):
     """A fresh library handle; `config` / `splits` force the plan for this handle,
-    `persistent` runs its ping-pong tiles with persistent blocks."""
+    `persistent` runs its ping-pong tiles with persistent blocks, `streamk`
+    (0 / 1 / 2) sets its stream-K mode (default: the plan rule)."""
     from dense_gemm_nt_amd import Gemm
-    old = {k: os.environ.get(k) for k in ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_PERSIST")}
+    old = {k: os.environ.get(k) for k in ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_PERSIST", "GEMM_STREAMK")}
     try:
+        if streamk is not None:
+            os.environ["GEMM_STREAMK"] = str(streamk)
+        else:
+            os.environ.pop("GEMM_STREAMK", None)
         if config:
             os.environ["GEMM_CONFIG"] = config
         else:

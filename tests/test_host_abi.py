@@ -108,8 +108,18 @@ def test_plans_fit_the_machine(g, M, N, K):
     assert 0 < p["lds_bytes"] <= LDS_BYTES
     assert p["lds_bytes"] >= 2 * (bm + bn) * bk * 2 or p["lds_bytes"] % (16 * 1024) == 0
     assert p["tiles"] == -(-M // bm) * -(-N // bn)
-    assert p["workgroups"] == p["tiles"] * p["splits"]
     k_tiles = -(-K // bk)
+    if p["streamk"]:
+        # every workgroup an equal run of the tiles * k_tiles units, one 256 KB
+        # FP32 slot per tile segment it touches
+        units = p["tiles"] * k_tiles
+        G = min(256, units)
+        assert p["splits"] == 1 and p["workgroups"] == G
+        run = -(-units // G)
+        assert p["workspace_bytes"] == G * ((run - 1) // k_tiles + 2) * 256 * 256 * 4
+        assert p["workspace_bytes"] <= 128 << 20
+        return
+    assert p["workgroups"] == p["tiles"] * p["splits"]
     assert 1 <= p["splits"] <= max(1, k_tiles)
     if p["splits"] > 1:
         assert p["workspace_bytes"] == p["splits"] * M * N * 4
@@ -126,7 +136,14 @@ def test_plan_regimes(g):
     assert g.gemm_plan(8192, 8192, 8192)["tiles"] == 1024
     # decode with few tiles splits K to cover the compute units
     p = g.gemm_plan(256, 8192, 8192)
-    assert p["splits"] > 1 and p["workgroups"] >= 128
+    assert (p["splits"] > 1 or p["streamk"]) and p["workgroups"] >= 128
+    # few big tiles with a long K: stream-K over all 256 compute units; with a
+    # short K (runs under 32 k-slabs) or a well-filled split plan, not
+    p = g.gemm_plan(3000, 3000, 5000)
+    assert p["streamk"] == 1 and p["workgroups"] == 256 and p["splits"] == 1
+    assert g.gemm_plan(3000, 3000, 3000)["streamk"] == 0
+    assert g.gemm_plan(256, 28672, 8192)["streamk"] == 0
+    assert g.gemm_plan(4096, 4096, 4096)["streamk"] == 0
     # mid-size M with a long K: the 256x256 tile with K splits fills the machine
     p = g.gemm_plan(512, 8192, 8192)
     assert p["name"] == "256x256x64_w8_pp2" and p["splits"] > 1 and p["workgroups"] >= 128
