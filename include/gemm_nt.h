@@ -66,10 +66,12 @@ typedef enum {
     GEMM_ERR_HIP = 5          /* a HIP runtime call or a launch failed */
 } gemm_status_t;
 
-/* Create a handle on the current device: allocates the split-K workspace
- * (128 MiB by default; GEMM_WORKSPACE_MB overrides).  *out is NULL on error.
- * For measurement, GEMM_CONFIG=<name> forces one kernel configuration and
- * GEMM_SPLITS=<n> a K split on every call of this handle; a GEMM_CONFIG that
+/* Create a handle on the current device: allocates the workspace for split-K
+ * and stream-K partials (128 MiB by default; GEMM_WORKSPACE_MB overrides).
+ * *out is NULL on error.  For measurement, GEMM_CONFIG=<name> forces one kernel
+ * configuration, GEMM_SPLITS=<n> a K split on every call of this handle, and
+ * GEMM_STREAMK=0/1/2 turns stream-K off, leaves it to the plan (default) or
+ * uses it whenever the 256 x 256 ping-pong tile is planned; a GEMM_CONFIG that
  * names no configuration makes gemm_create return GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_create(gemm_handle_t *out);
 
