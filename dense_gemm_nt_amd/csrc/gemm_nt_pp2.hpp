@@ -321,13 +321,15 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // One memory phase: the 8 loads of slab `li` (if has_load), then the 24
         // fragment reads of slab i.  Loads first: their issue is what the vector
         // memory unit paces, and the reads overlap it.
-        auto memory_phase = [&](auto grp, int i, bool has_load, int li, auto nt) {
+        auto memory_phase = [&](auto grp, int i, bool has_load, int li, auto nt, bool reads = true) {
             if (has_load)
                 issue_loads(grp, li, nt);
+            if (reads) {
     #pragma unroll
-            for (int r = 0; r < 24; ++r)
-                read_one(grp, i, r);
-            scale_read(grp, i);
+                for (int r = 0; r < 24; ++r)
+                    read_one(grp, i, r);
+                scale_read(grp, i);
+            }
         };
         auto compute_slab = [&]() {
             if constexpr (!F8) {
@@ -396,6 +398,12 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         using G0 = std::integral_constant<int, 0>;
         using G1 = std::integral_constant<int, 1>;
 
+        // Group 1 owns tile rows 128..255.  When all of them lie past M (a
+        // grouped problem with few tokens, the last tile row of a ragged M) its
+        // waves skip their fragment reads and MFMAs: they still load A for group
+        // 0 and keep every barrier, and their accumulators, never stored, stay 0.
+        // (Not in the persistent kernel, whose registers it would overflow.)
+        const bool g1_rows = PS || m0 + 128 < p.M;
         if (nk > 0) {
             // Prologue: B(0) by group 0; A(0), A(1) by group 1.  Slab 0 lands before
             // phase 0; A(1) by the end of phase 1 (the steady-state wait).
@@ -442,13 +450,13 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             } else {
                 for (int i = 0; i < nk; ++i) {
                     GNT_PP2_EVENT(i, 0);
-                    if (i > 0)
+                    if (i > 0 && g1_rows)
                         compute_slab();                        // slab i-1
                     __builtin_amdgcn_sched_barrier(0);
                     GNT_PP2_EVENT(i, 1);
                     phase_end();                               // end of phase 2i
                     GNT_PP2_EVENT(i, 2);
-                    memory_phase(G1{}, i, i + 2 < nk, i + 2, std::false_type{});   // A(i+2)
+                    memory_phase(G1{}, i, i + 2 < nk, i + 2, std::false_type{}, g1_rows);   // A(i+2)
                     wait_lgkmcnt0();
                     GNT_PP2_EVENT(i, 3);
                     if (i + 2 < nk)                            // A(i+1) landed
@@ -458,7 +466,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     GNT_PP2_EVENT(i, 4);
                     phase_end();                               // end of phase 2i+1
                 }
-                compute_slab();                                // slab nk-1
+                if (g1_rows)
+                    compute_slab();                            // slab nk-1
             }
         }
 
