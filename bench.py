@@ -120,11 +120,20 @@ def spot_check(bufs, idx, shapes, in_dt, out_dt, dist):
     return max(w1, w2)
 
 
-def _event_time(launch, iters, warmup, stream):
+def _event_time(launch, iters, warmup, stream, settle_s=0.3):
     """Average duration of `launch()` over `iters` back-to-back calls on `stream`
-    (HIP events on that stream), after `warmup` calls."""
+    (HIP events on that stream), after a settle phase (launches for `settle_s`
+    seconds, as before the primary timing: a GPU that sat idle runs its first
+    launches at a lower clock) and `warmup` calls."""
     import torch
     with torch.cuda.stream(stream):
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < settle_s:
+            launch()
+            n += 1
+            if n % 10 == 0:
+                torch.cuda.synchronize()
         for _ in range(warmup):
             launch()
         torch.cuda.synchronize()
