@@ -53,6 +53,29 @@ def trace_groups(path):
     return groups
 
 
+def leading_run(path, name, workgroups):
+    """Durations (ns) of the first unbroken run of dispatches of one kernel at one
+    grid size, in dispatch order: the workload a bench step times first, before
+    later workloads launch the same kernel at the same grid."""
+    rows = []
+    for r in _rows(path):
+        wg = int(r.get("Workgroup_Size_X") or 1) * int(r.get("Workgroup_Size_Y") or 1) * \
+            int(r.get("Workgroup_Size_Z") or 1)
+        grid = int(r.get("Grid_Size_X") or 0) * int(r.get("Grid_Size_Y") or 1) * \
+            int(r.get("Grid_Size_Z") or 1)
+        rows.append((int(r["Start_Timestamp"]), r.get("Kernel_Name") or "?", grid // max(wg, 1),
+                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    run, started = [], False
+    for _, n, g, d in rows:
+        if n == name and g == workgroups:
+            run.append(d)
+            started = True
+        elif started and "copyBuffer" not in n and "elementwise" not in n:
+            break
+    return run
+
+
 def counters(path, skip):
     per = defaultdict(lambda: defaultdict(list))   # kernel -> counter -> values in dispatch order
     order = OrderedDict()
