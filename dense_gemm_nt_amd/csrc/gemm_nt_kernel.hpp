@@ -190,12 +190,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
             const int s = i % STAGES;
             // Slab i landed for this wave once at most (STAGES-2) newer slabs are in flight.
             if (i + STAGES - 2 < nkt) {
-                if constexpr (STAGES == 2)
-                    wait_vmcnt<0>();
-                else if constexpr (STAGES == 3)
-                    wait_vmcnt<(A_LOADS + B_LOADS)>();
-                else
-                    wait_vmcnt<2 * (A_LOADS + B_LOADS)>();
+                static_assert((STAGES - 2) * (A_LOADS + B_LOADS) <= 63, "vmcnt range");
+                wait_vmcnt<(STAGES - 2) * (A_LOADS + B_LOADS)>();
             } else {
                 wait_vmcnt<0>();
             }

@@ -16,7 +16,7 @@ typedef launch_fn LaunchTable[2][3];
 
 // kernel-template tiles (gemm_nt_kernel.hpp), in the order of their names
 extern LaunchTable kTile256x256_w4_s2, kTile256x128_w4_s3, kTile128x128_w4_s4,
-    kTile32x256_w4_s4, kTile128x128_w4_s4_kmask, kTile128x128_w4_s2;
+    kTile32x256_w4_s4, kTile128x128_w4_s4_kmask, kTile128x128_w4_s2, kTile32x128_w4_s6;
 // the 256x256 ping-pong kernels (gemm_nt_pingpong.hpp, gemm_nt_pp2.hpp); the
 // pp2 tables by operand layout: K-major A and B (NT), MN-major B, MN-major A,
 // both MN-major

@@ -28,6 +28,7 @@ LaunchTable kTile128x128_w4_s4 = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, false);
 LaunchTable kTile32x256_w4_s4 = GNT_TILE_TABLE(32, 256, 64, 1, 4, 4, false);
 LaunchTable kTile128x128_w4_s4_kmask = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, true);
 LaunchTable kTile128x128_w4_s2 = GNT_TILE_TABLE(128, 128, 64, 2, 2, 2, false);
+LaunchTable kTile32x128_w4_s6 = GNT_TILE_TABLE(32, 128, 64, 1, 4, 6, false);
 #endif
 
 }  // namespace gnt

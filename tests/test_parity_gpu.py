@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 CONFIGS = ["256x256x64_w4_s2", "256x128x64_w4_s3", "128x128x64_w4_s4", "32x256x64_w4_s4",
            "128x128x64_w4_s4_kmask", "256x256x64_w8_pingpong",
-           "256x256x64_w8_pp2", "128x128x64_w4_s2"]
+           "256x256x64_w8_pp2", "128x128x64_w4_s2", "32x128x64_w4_s6"]
 
 
 @pytest.fixture(scope="module")
