@@ -150,6 +150,18 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         const int64_t big = std::max<int64_t>(1, cdiv(M, 256) * cdiv(N, 256));
         const int64_t ksplit = std::min<int64_t>(kNumCUs / big, cdiv(K, 64) / 20);
         cfg = big * std::max<int64_t>(1, ksplit) >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_W4_128x128;
+        // Small squares: the 32x128 tile, when without K splits it fills at
+        // least as many compute units (in one pass) as the 128x128 tile does with
+        // the splits the rule below gives it; it then needs no partials.
+        if (cfg == CFG_W4_128x128) {
+            const int64_t t128 = cdiv(M, 128) * cdiv(N, 128), t32 = cdiv(M, 32) * cdiv(N, 128);
+            const int64_t kt = cdiv(K, 64);
+            int64_t s128 = 1;
+            if (t128 < kNumCUs && kt >= 16)
+                s128 = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / t128, kt / 8));
+            if (t32 <= kNumCUs && t32 >= t128 * s128)
+                cfg = CFG_W4_32x128;
+        }
     }
     // 128x128 tiles that overflow one pass of the machine but fit two: the
     // two-stage ring (64 KB of LDS) lets two blocks share a compute unit, so
@@ -184,11 +196,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         if (splits < 1)
             splits = 1;
     }
-    // The 32-row tile streams B rows whose K splits start kt_per_split * 128
-    // bytes apart.  Starts a multiple of 4 KB apart measured up to 20% slower
-    // (the blocks of one B row then hit the same DRAM channels together), so the
-    // nearest split count with another stride is taken instead.
-    if (cfg == CFG_W4_32x128 && force_splits <= 0 && p.k_tiles >= 16) {
+    // For M <= 32 the 32-row tile streams B rows whose K splits start
+    // kt_per_split * 128 bytes apart.  Starts a multiple of 4 KB apart measured
+    // up to 20% slower (the blocks of one B row then hit the same DRAM channels
+    // together), so the nearest split count with another stride is taken.
+    if (cfg == CFG_W4_32x128 && M <= 32 && force_splits <= 0 && p.k_tiles >= 16) {
         auto aliased = [&](int sp) { return (cdiv(p.k_tiles, sp) * c.bk * 2) % 4096 == 0; };
         auto ok = [&](int sp) { return sp >= 1 && sp <= 8 && p.k_tiles / sp >= 8 && !aliased(sp); };
         if (aliased(splits)) {
