@@ -134,7 +134,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         cfg = force_cfg;
     } else if (K % 8) {
         cfg = CFG_W4_128x128_KMASK;
-    } else if (M <= 32) {
+    } else if (M <= 64) {
+        // (at M = 64, two 32-row tiles per column still beat one 128-row tile:
+        // 39.2 -> 36.8 us at 64x8192x8192, 19.9 -> 15.3 at 64x4096x4096; from
+        // M = 96 the 128x128 tile is faster by half)
         cfg = CFG_W4_32x128;
     } else if (M <= 128) {
         cfg = CFG_W4_128x128;
