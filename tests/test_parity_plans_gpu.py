@@ -1,0 +1,65 @@
+"""Every output element against the oracle on seeded shapes drawn from each
+regime of the planner, through the default plan (no forced configuration):
+small M with stride-aware K splits, small squares on the 32x128 tile, the
+128x128 tiles (one or two blocks per compute unit), the 256x256 ping-pong tile
+with and without K splits.  The shapes are drawn once from a fixed seed, so a
+failure names a shape that reproduces.  Bound: tests/tolerance.py.
+"""
+import numpy as np
+import pytest
+
+from dense_gemm_nt_amd import gemm_plan, _lib
+from gemm_inputs import make_operands
+from tests.gpu_util import compare_full, new_handle, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+CODE = {"bf16": _lib.GEMM_BF16, "fp16": _lib.GEMM_FP16, "fp32": _lib.GEMM_FP32}
+
+
+def _shapes():
+    rng = np.random.default_rng(20261202)
+    regimes = [
+        # (M range, N range, K range): small M with long K (K splits); small
+        # squares; 96 < M <= 128 (128x128 tile with K splits); 128x128 tiles
+        # just past one pass of the machine (two blocks per compute unit);
+        # decode-like 128 < M <= 256 (ping-pong tile, K splits); mid squares
+        ((1, 64), (100, 1200), (1024, 4096)),
+        ((257, 700), (257, 700), (64, 1100)),
+        ((97, 128), (2000, 6000), (512, 2048)),
+        ((990, 1020), (4100, 4300), (256, 512)),
+        ((129, 256), (300, 1500), (2048, 6000)),
+        ((1500, 2100), (1500, 2100), (256, 768)),
+    ]
+    out = []
+    for (m0, m1), (n0, n1), (k0, k1) in regimes:
+        for _ in range(3):
+            M = int(rng.integers(m0, m1 + 1))
+            N = int(rng.integers(n0, n1 + 1))
+            K = int(rng.integers(k0 // 8, k1 // 8 + 1)) * 8
+            out.append((M, N, K))
+    return out
+
+
+SHAPES = _shapes()
+DTS = [("bf16", "bf16"), ("fp16", "fp32"), ("bf16", "fp32"), ("fp16", "fp16")]
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES)), ids=["%dx%dx%d" % s for s in SHAPES])
+def test_default_plan_every_element(i):
+    M, N, K = SHAPES[i]
+    ind, outd = DTS[i % len(DTS)]
+    p = gemm_plan(M, N, K, CODE[ind], CODE[outd])
+    say("case plan M=%d N=%d K=%d %s->%s %s splits=%d streamk=%d" % (
+        M, N, K, ind, outd, p["name"], p["splits"], p["streamk"]))
+    h = new_handle()
+    A, B = make_operands(M, N, K, ind, "uniform", seed=i)
+    C = run_gpu(h, A, B, K, ind, outd, ldc=N + (i % 3))
+    err, worst = compare_full(C, A, B, K, ind, outd, "M=%d N=%d K=%d" % (M, N, K))
+    say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
+    h.close()
+
+
+def test_the_draw_reaches_each_tile_family():
+    names = {gemm_plan(M, N, K)["name"] for M, N, K in SHAPES}
+    assert {"32x128x64_w4_s6", "128x128x64_w4_s4", "128x128x64_w4_s2", "256x256x64_w8_pp2"} <= names, names
