@@ -6,12 +6,16 @@ that are already resident in HBM.  Input sets rotate so the 256 MB last-level
 cache cannot hold them across steps (cold-cache numbers).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--quick]
+    python bench.py --all-configs [--config NAME ...]
 
 Primary workload: M = N = K = 4096, BF16 inputs uniform on [-1, 1), FP32
 accumulation, BF16 output.  A second line item in the same JSON object reports
 the decode-regime shape M = 256, N = 28672, K = 8192 (A ~ N(0,1), B ~ N(0, 0.02^2)),
-and an "extensions" list times the other forms of the product (operand
-layouts, fused epilogue, FP8 with scales, grouped launch) on their workloads.
+an "extensions" list times the other forms of the product (operand
+layouts, fused epilogue, FP8 with scales, grouped launch) on their workloads,
+and a "configs" list gives every configured workload (CONFIGS below): median,
+p10 and p90 of 50 launches each between HIP events, its roofline fraction and
+an oracle spot check.  --all-configs prints only those, one JSON line each.
 """
 from __future__ import annotations
 
@@ -100,15 +104,16 @@ def time_gemm(g, shapes, steps, warmup, sets, in_dt, out_dt, dist):
     return wall_ms, event_ms, bufs, last, settle
 
 
-def spot_check(bufs, idx, shapes, in_dt, out_dt, dist):
-    """Oracle on two rows and 2000 points of the last timed output."""
+def spot_check(bufs, idx, shapes, in_dt, out_dt, dist, seed=None):
+    """Oracle on two rows and 2000 points of the output bufs[idx][2], made from
+    the input set drawn with `seed` (default: idx)."""
     import numpy as np
     import oracle
     from gemm_inputs import make_operands
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from tests.tolerance import check
     M, N, K = shapes
-    A, B = make_operands(M, N, K, in_dt, dist, seed=idx)
+    A, B = make_operands(M, N, K, in_dt, dist, seed=idx if seed is None else seed)
     C = bufs[idx][2].float().cpu().double().numpy()
     rows = [0, M - 1]
     Cr, S = oracle.gemm_nt_rows(A, B, rows, K=K, in_dtype=in_dt)
@@ -254,6 +259,133 @@ def extensions(g, iters=30, warmup=10):
     return res
 
 
+# Every configured workload: (name, M, N, K, in, out, values, rotating input
+# sets).  The sets rotate so that the operands of one launch are not in the
+# 256 MB last-level cache from the launch before (sets x algorithmic bytes
+# >= 512 MB, or one set when a single one is larger).
+CONFIGS = [
+    ("square512", 512, 512, 512, "bf16", "fp32", "uniform", 8),
+    ("square4096", 4096, 4096, 4096, "bf16", "bf16", "uniform", 6),
+    ("square4096_fp16", 4096, 4096, 4096, "fp16", "bf16", "uniform", 6),
+    ("prefill8192", 8192, 8192, 8192, "bf16", "bf16", "llm", 2),
+    ("prefill_mlp_up", 8192, 28672, 8192, "bf16", "bf16", "llm", 1),
+    ("decode_mlp_up", 256, 28672, 8192, "bf16", "bf16", "llm", 2),
+    ("decode_mlp_down", 256, 8192, 28672, "bf16", "bf16", "llm", 2),
+    ("decode_qkv", 256, 10240, 8192, "bf16", "bf16", "llm", 3),
+    ("decode_attn_out", 256, 8192, 8192, "bf16", "bf16", "llm", 4),
+    ("ragged_1000x4097x1536", 1000, 4097, 1536, "fp16", "fp32", "uniform", 16),
+    ("ragged_127x28672x8192", 127, 28672, 8192, "fp16", "fp32", "uniform", 2),
+    ("ragged_3000x3000x5000", 3000, 3000, 5000, "fp16", "fp32", "uniform", 6),
+    ("ragged_1x8192x8192", 1, 8192, 8192, "fp16", "fp32", "uniform", 4),
+]
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    pos = (len(xs) - 1) * q
+    lo = int(pos)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (pos - lo)
+
+
+def time_config(g, cfg, iters=50, warmup=10, check=True):
+    """One configured workload: `iters` launches, each between two HIP events on
+    the launch stream, after a 0.3 s settle phase and `warmup` launches.  Returns
+    median / p10 / p90 of the per-launch times, the batch mean (first to last
+    event), TFLOP/s and roofline fraction at the median, the plan, and an oracle
+    spot check (two whole rows and 2000 points of the last output)."""
+    import torch
+    from gemm_inputs import make_operands
+    from dense_gemm_nt_amd import roofline
+
+    if args.all_configs:
+        for cfg in CONFIGS:
+            if args.config and cfg[0] not in args.config:
+                continue
+            print(json.dumps(time_config(g, cfg, check=not args.no_check)), flush=True)
+        return
+    name, M, N, K, in_dt, out_dt, dist, sets = cfg
+    dev = torch.device("cuda", 0)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+    code = {"bf16": 0, "fp16": 1, "fp32": 2}
+    bufs = []
+    for i in range(sets):
+        A, B = make_operands(M, N, K, in_dt, dist, seed=i)
+        bufs.append((A.to(dev), B.to(dev), torch.empty((M, N), dtype=tdt[out_dt], device=dev)))
+        del A, B
+    h = g.Gemm()
+    stream = torch.cuda.Stream(device=dev)
+    sp = stream.cuda_stream
+    n_launch = [0]
+
+    def launch():
+        A, B, C = bufs[n_launch[0] % sets]
+        h.run_raw(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, K, K, N,
+                  code[in_dt], code[out_dt], sp)
+        n_launch[0] += 1
+
+    with torch.cuda.stream(stream):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            for _ in range(10):
+                launch()
+            torch.cuda.synchronize()
+        for _ in range(warmup):
+            launch()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+        torch.cuda.synchronize()
+    us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    batch_us = ev[0][0].elapsed_time(ev[-1][1]) * 1e3 / iters
+    last = (n_launch[0] - 1) % sets
+    plan = g.gemm_plan(M, N, K, code[in_dt], code[out_dt])
+    r = roofline.roofline(M, N, K, 2, 4 if out_dt == "fp32" else 2, peak_tflops=PEAK_TFLOPS,
+                          hbm_tbs=HBM_TBS)
+    med = _pct(us, 0.5)
+    flops = 2.0 * M * N * K
+    floor_us = max(flops / (PEAK_TFLOPS * 1e12), r.bytes / (HBM_TBS * 1e12)) * 1e6
+    rec = {"config": name, "M": M, "N": N, "K": K, "in": in_dt, "out": out_dt, "values": dist,
+           "sets": sets, "iters": iters,
+           "median_us": round(med, 2), "p10_us": round(_pct(us, 0.1), 2),
+           "p90_us": round(_pct(us, 0.9), 2), "batch_mean_us": round(batch_us, 2),
+           "tflops": round(flops / (med * 1e-6) / 1e12, 1),
+           "pct_mfma_peak": round(100 * flops / (med * 1e-6) / 1e12 / PEAK_TFLOPS, 2),
+           "bound": r.bound, "floor_us": round(floor_us, 2),
+           "roofline_frac": round(floor_us / med, 4),
+           "plan": {"name": plan["name"], "splits": plan["splits"], "streamk": plan["streamk"],
+                    "workgroups": plan["workgroups"]}}
+    if r.bound == "hbm":
+        rec["gbs"] = round(r.bytes / (med * 1e-6) / 1e9, 1)
+    if check:
+        t0 = time.perf_counter()
+        rec["parity_worst_err_over_bound"] = round(
+            spot_check([(None, None, bufs[last][2])], 0, (M, N, K), in_dt, out_dt, dist,
+                       seed=last), 4)
+        rec["oracle_check_s"] = round(time.perf_counter() - t0, 2)
+    h.close()
+    del bufs
+    torch.cuda.empty_cache()
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shapes, in_dt, dist, target_s=10.0):
     """The oracle as it is, on whole rows of the same workload, on this host's
     cores: about `target_s` seconds of work (more rows, or repeats of the whole
@@ -286,7 +418,27 @@ def cpu_baseline(shapes, in_dt, dist, target_s=10.0):
         sample = "the whole %dx%dx%d product (%.1f GFLOP), %d time%s in %.1f s" % (
             M, N, K, flops / 1e9, reps, "s" if reps > 1 else "", dt * reps)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": sample}
+            "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
+            "per_core": per_core_rate()}
+
+
+def per_core_rate():
+    """The oracle on one thread (a child process with OMP_NUM_THREADS=1): the
+    whole 512^3 BF16 product, GFLOP/s per core."""
+    import subprocess
+    code = ("import time, sys; sys.path.insert(0, %r); import oracle; "
+            "from gemm_inputs import make_operands; "
+            "A, B = make_operands(512, 512, 512, 'bf16', 'uniform', seed=0); "
+            "oracle.gemm_nt(A[:8], B); t = time.perf_counter(); oracle.gemm_nt(A, B); "
+            "print(2 * 512 ** 3 / (time.perf_counter() - t) / 1e9, oracle.num_threads())" % ROOT)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
+                             text=True, timeout=120, check=True).stdout.split()
+        return {"gflops": round(float(out[0]), 3), "threads": int(out[1]),
+                "sample": "the whole 512^3 bf16 product"}
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
 
 
 def main():
@@ -297,6 +449,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the parity spot check")
     ap.add_argument("--quick", action="store_true", help="primary workload only")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one JSON line per configured workload (median / p10 / p90 of 50 "
+                         "event-timed launches each), then exit")
+    ap.add_argument("--config", action="append", default=[],
+                    help="with --all-configs: only the named workload(s)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GEMM has no multi-GPU path here "
@@ -376,6 +533,8 @@ def main():
     if not args.quick:
         out["extensions"] = extensions(g)
         torch.cuda.empty_cache()
+        # every configured workload, 50 event-timed launches each
+        out["configs"] = [time_config(g, cfg, check=not args.no_check) for cfg in CONFIGS]
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shapes, "bf16", "uniform")

@@ -14,12 +14,12 @@ CSRC = os.path.join(PKG, "csrc")
 # the host side and one translation unit per group of kernel instantiations,
 # compiled in parallel and linked into one shared library
 SOURCES = [os.path.join(CSRC, f) for f in (
-    "gemm_nt.hip", "launch_tiles_a.hip", "launch_tiles_b.hip", "launch_pingpong.hip",
+    "gemm_nt.hip", "launch_tiles_a.hip", "launch_tiles_b.hip",
     "launch_pp2.hip", "launch_pp2_km.hip", "launch_pp2_mk.hip", "launch_pp2_mm.hip",
     "launch_pp2_f8_e4e4.hip", "launch_pp2_f8_e4e5.hip", "launch_pp2_f8_e5e4.hip",
     "launch_pp2_f8_e5e5.hip", "launch_pp2_grouped.hip", "launch_pp2_persistent.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp",
-                                           "gemm_nt_pingpong.hpp", "gemm_nt_pp2.hpp",
+                                           "gemm_nt_pp2.hpp",
                                            "gemm_nt_launch.hpp", "launch_pp2.hip",
                                            "launch_pp2_f8.hip", "launch_tiles_a.hip")] + \
     [os.path.join(ROOT, "include", "gemm_nt.h")]

@@ -76,27 +76,19 @@ struct Config {
 // 32x32 MFMA tiles.  Configurations with kmask = 1 zero the operand columns past
 // K in registers and are the only ones planned when K is not a multiple of 8.
 const Config kConfigs[] = {
-    {"256x256x64_w4_s2", 256, 256, 64, 4, 2, 131072, 0, 1, gnt::kTile256x256_w4_s2},
-    {"256x128x64_w4_s3", 256, 128, 64, 4, 3, 147456, 0, 1, gnt::kTile256x128_w4_s3},
     {"128x128x64_w4_s4", 128, 128, 64, 4, 4, 131072, 0, 1, gnt::kTile128x128_w4_s4},
-    {"32x256x64_w4_s4", 32, 256, 64, 4, 4, 147456, 0, 1, gnt::kTile32x256_w4_s4},
     {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 131072, 1, 1, gnt::kTile128x128_w4_s4_kmask},
-    {"256x256x64_w8_pingpong", 256, 256, 64, 8, 2, 131072, 0, 1, gnt::kPingpong256},
     {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk},
     {"128x128x64_w4_s2", 128, 128, 64, 4, 2, 65536, 0, 1, gnt::kTile128x128_w4_s2},
     {"32x128x64_w4_s6", 32, 128, 64, 4, 6, 122880, 0, 1, gnt::kTile32x128_w4_s6},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
-    CFG_W4_256x256 = 0,
-    CFG_W4_256x128 = 1,
-    CFG_W4_128x128 = 2,
-    CFG_W4_32x256 = 3,
-    CFG_W4_128x128_KMASK = 4,
-    CFG_PP_256x256 = 5,
-    CFG_PP2_256x256 = 6,
-    CFG_W4_128x128_S2 = 7,
-    CFG_W4_32x128 = 8,
+    CFG_W4_128x128 = 0,
+    CFG_W4_128x128_KMASK = 1,
+    CFG_PP2_256x256 = 2,
+    CFG_W4_128x128_S2 = 3,
+    CFG_W4_32x128 = 4,
 };
 
 struct Plan {
@@ -203,7 +195,9 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     // kt_per_split * 128 bytes apart.  Starts a multiple of 4 KB apart measured
     // up to 20% slower (the blocks of one B row then hit the same DRAM channels
     // together), so the nearest split count with another stride is taken.
-    if (cfg == CFG_W4_32x128 && M <= 32 && force_splits <= 0 && p.k_tiles >= 16) {
+    // Only when the fill rule split K: with one split no two blocks start in
+    // the same B row.
+    if (cfg == CFG_W4_32x128 && M <= 32 && force_splits <= 0 && p.k_tiles >= 16 && splits > 1) {
         auto aliased = [&](int sp) { return (cdiv(p.k_tiles, sp) * c.bk * 2) % 4096 == 0; };
         auto ok = [&](int sp) { return sp >= 1 && sp <= 8 && p.k_tiles / sp >= 8 && !aliased(sp); };
         if (aliased(splits)) {

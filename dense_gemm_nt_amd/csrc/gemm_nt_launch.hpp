@@ -15,12 +15,11 @@ typedef hipError_t (*launch_fn)(const KernelArgs &, unsigned grid, hipStream_t);
 typedef launch_fn LaunchTable[2][3];
 
 // kernel-template tiles (gemm_nt_kernel.hpp), in the order of their names
-extern LaunchTable kTile256x256_w4_s2, kTile256x128_w4_s3, kTile128x128_w4_s4,
-    kTile32x256_w4_s4, kTile128x128_w4_s4_kmask, kTile128x128_w4_s2, kTile32x128_w4_s6;
-// the 256x256 ping-pong kernels (gemm_nt_pingpong.hpp, gemm_nt_pp2.hpp); the
-// pp2 tables by operand layout: K-major A and B (NT), MN-major B, MN-major A,
+extern LaunchTable kTile128x128_w4_s4, kTile128x128_w4_s4_kmask, kTile128x128_w4_s2,
+    kTile32x128_w4_s6;
+// the 256x256 ping-pong kernel (gemm_nt_pp2.hpp), by operand layout: K-major A and B (NT), MN-major B, MN-major A,
 // both MN-major
-extern LaunchTable kPingpong256, kPP2_kk, kPP2_km, kPP2_mk, kPP2_mm;
+extern LaunchTable kPP2_kk, kPP2_km, kPP2_mk, kPP2_mm;
 // FP8 inputs on the same kernel, one table per (A format, B format) with E4M3
 // = e4 and E5M2 = e5, indexed [scale mode (per tensor, blockwise)][out dtype]
 extern LaunchTable kPP2_f8_e4e4, kPP2_f8_e4e5, kPP2_f8_e5e4, kPP2_f8_e5e5;

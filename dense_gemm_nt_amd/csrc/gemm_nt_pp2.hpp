@@ -1,13 +1,12 @@
 // gemm_nt_pp2.hpp -- eight-wave 256x256x64 ping-pong tile in which both wave
 // groups issue global loads, over an LDS ring of 16 KB units (gfx950).
 //
-// The phase structure is the one of gemm_nt_pingpong.hpp: two groups of four
-// waves (one wave of each group per SIMD) alternate between a memory phase
-// (LDS -> register fragment reads, plus direct-to-LDS global loads) and a
-// compute phase (the 32 MFMAs of one 64-deep k-slab), and a workgroup barrier
-// ends every phase.  What changes is who loads.  Issuing the 64 wave-wide
-// 1 KB loads of a slab takes longer than one compute phase when a single group
-// issues all of them: the vector memory unit accepts a wave-wide 16-byte-per-
+// Two groups of four waves (one wave of each group per SIMD) alternate between
+// a memory phase (LDS -> register fragment reads, plus direct-to-LDS global
+// loads) and a compute phase (the 32 MFMAs of one 64-deep k-slab), and a
+// workgroup barrier ends every phase.  Both groups load.  Issuing the 64
+// wave-wide 1 KB loads of a slab takes longer than one compute phase when a
+// single group issues all of them: the vector memory unit accepts a wave-wide 16-byte-per-
 // lane load every ~25 cycles, so the loading waves stall on issue, not on
 // latency.  Here each group issues half a slab in its own memory phase, while
 // the other group keeps the matrix cores busy ("A Blackwell GEMM by Hand in

@@ -162,6 +162,12 @@ def test_plan_regimes(g):
     assert p["name"] == "32x128x64_w4_s6" and p["splits"] == 3
     assert g.gemm_plan(64, 8192, 8192)["name"] == "32x128x64_w4_s6"
     assert g.gemm_plan(96, 28672, 8192)["name"] == "128x128x64_w4_s4"
+    # the 4 KB stride rule only moves a split count the fill rule chose: with
+    # at least 256 tiles there is one split, and it stays one
+    p = g.gemm_plan(1, 65536, 8192)
+    assert p["name"] == "32x128x64_w4_s6" and p["tiles"] == 512 and p["splits"] == 1
+    p = g.gemm_plan(32, 32768, 8192)
+    assert p["tiles"] == 256 and p["splits"] == 1
 
 
 def test_run_layout_rejects_null_handle_before_any_device_work(g):

@@ -132,3 +132,56 @@ def test_int3_recipe_is_exact_small_integers_and_powers_of_two():
     for s in (sa, sb):
         e = np.log2(s.numpy())
         assert np.array_equal(e, np.round(e))
+
+
+def _check_points(points_fn, fa, fb, mode, block_m):
+    # fp8.gemm_points is the checker of the full-size FP8 tests: at every point
+    # it equals fp8.gemm within the binary64 summation bound K 2^-53 S (the two
+    # sum in different orders), and, at a few points, the exact rational sum.
+    # M, N span two row blocks and two column blocks, K a ragged third k-block.
+    M, N, K = 140, 131, 272
+    A, B, sa, sb = make_fp8_operands(M, N, K, fa, fb, "uniform", seed=6, mode=mode,
+                                     block_m=block_m)
+    C, S = fp8.gemm(A, B, K=K, fmt_a=fa, fmt_b=fb, mode=mode, scale_a=sa, scale_b=sb,
+                    block_m=block_m)
+    rng = np.random.default_rng(3)
+    ii = np.concatenate([rng.integers(0, M, 300), [0, 139, 5, 130, 130, 5]])
+    jj = np.concatenate([rng.integers(0, N, 300), [130, 0, 130, 5, 127, 127]])
+    Cp, Sp = points_fn(A, B, ii, jj, K=K, fmt_a=fa, fmt_b=fb, mode=mode, scale_a=sa,
+                       scale_b=sb, block_m=block_m, chunk=64)
+    bound = K * 2.0 ** -53 * S[ii, jj]
+    assert np.all(np.abs(Cp - C[ii, jj]) <= bound)
+    assert np.all(np.abs(Sp - S[ii, jj]) <= bound)
+    for i, j, c in zip(ii[-6:], jj[-6:], Cp[-6:]):
+        sai = sa[i // block_m:i // block_m + 1] if mode == "block" else sa
+        sbj = sb[j // 128:j // 128 + 1] if mode == "block" else sb
+        Ce, Se = _exact(A[i:i + 1], B[j:j + 1], K, fa, fb, mode, sai, sbj, block_m)
+        assert abs(Fraction(float(c)) - Ce[0][0]) <= Fraction(K) * Fraction(2) ** -52 * Se[0][0]
+
+
+@pytest.mark.parametrize("fa,fb,mode,block_m", [("e4m3", "e4m3", "tensor", 1),
+                                                ("e4m3", "e4m3", "block", 1),
+                                                ("e5m2", "e4m3", "block", 128),
+                                                ("e4m3", "e5m2", "block", 1)])
+def test_points_agree_with_full_product(fa, fb, mode, block_m):
+    _check_points(fp8.gemm_points, fa, fb, mode, block_m)
+
+
+def _swapped_points(A, B, ii, jj, **kw):
+    return fp8.gemm_points(A, B, jj, ii, **kw)
+
+
+def _swapped_formats(A, B, ii, jj, fmt_a, fmt_b, **kw):
+    return fp8.gemm_points(A, B, ii, jj, fmt_a=fmt_b, fmt_b=fmt_a, **kw)
+
+
+def _wrong_block_rows(A, B, ii, jj, block_m, **kw):
+    return fp8.gemm_points(A, B, ii, jj, block_m=128 if block_m == 1 else 1, **kw)
+
+
+@pytest.mark.parametrize("mutant", [_swapped_points, _swapped_formats, _wrong_block_rows])
+def test_points_pin_catches_planted_mistakes(mutant):
+    # exchanged coordinates, exchanged operand formats, or the other row-block
+    # size of A's scales: each fails the pin above (a shape error counts too)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _check_points(mutant, "e5m2", "e4m3", "block", 1)

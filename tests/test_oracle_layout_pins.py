@@ -103,3 +103,61 @@ def test_make_stored_keeps_the_values():
                            A.view(torch.int16))
         assert torch.equal(torch.from_numpy(oracle.logical_operand(Xb, lb).view(np.int16)),
                            B.view(torch.int16))
+
+
+def _storage_loop(Xa, Xb, la, lb, lda, ldb, i, j, K):
+    """sum_k a(i, k) b(j, k) read straight from the flat storage offsets."""
+    fa = Xa.double().numpy().ravel()
+    fb = Xb.double().numpy().ravel()
+    acc = 0.0
+    for k in range(K):
+        ai = fa[i * lda + k] if la == "k" else fa[k * lda + i]
+        bj = fb[j * ldb + k] if lb == "k" else fb[k * ldb + j]
+        acc += ai * bj
+    return acc
+
+
+def _check_points(points_fn, la, lb):
+    # oracle.gemm_points is the checker of the full-size layout tests: at every
+    # point it must equal oracle.gemm bitwise (same per-element sum) and the
+    # plain loop over storage offsets.  M != N and points on both sides of the
+    # diagonal, including (i, j) and (j, i) pairs, so exchanged coordinates or
+    # operands change the values; padded leading dimensions hold NaN.
+    M, N, K = 37, 23, 40
+    A, B = make_operands(M, N, K, "bf16", "uniform", seed=21)
+    lda = (K if la == "k" else M) + 8
+    ldb = (K if lb == "k" else N) + 8
+    Xa, Xb = store(A, la, lda), store(B, lb, ldb)
+    Va = Xa[:, :K] if la == "k" else Xa[:, :M]
+    Vb = Xb[:, :K] if lb == "k" else Xb[:, :N]
+    full, S = oracle.gemm(Va, Vb, la, lb, in_dtype="bf16")
+    rng = np.random.default_rng(5)
+    ii = list(rng.integers(0, M, 60)) + [0, M - 1, 3, 17, 17, 3]
+    jj = list(rng.integers(0, N, 60)) + [N - 1, 0, 17, 3, 22, 22]
+    Cp, Sp = points_fn(Va, Vb, ii, jj, la, lb, in_dtype="bf16")
+    assert np.array_equal(Cp, full[ii, jj]) and np.array_equal(Sp, S[ii, jj])
+    loop = np.array([_storage_loop(Xa, Xb, la, lb, lda, ldb, i, j, K) for i, j in zip(ii, jj)])
+    assert np.allclose(Cp, loop, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_points_agree_with_full_product_and_storage_loop(la, lb):
+    _check_points(oracle.gemm_points, la, lb)
+
+
+def _swapped_points(Va, Vb, ii, jj, la, lb, in_dtype):
+    C, S = oracle.gemm_points(Va, Vb, jj, ii, la, lb, in_dtype=in_dtype)
+    return C, S
+
+
+def _swapped_layouts(Va, Vb, ii, jj, la, lb, in_dtype):
+    return oracle.gemm_points(Va, Vb, ii, jj, lb, la, in_dtype=in_dtype)
+
+
+@pytest.mark.parametrize("mutant", [_swapped_points, _swapped_layouts])
+def test_points_pin_catches_planted_mistakes(mutant):
+    # the pin above fails for a points function with exchanged coordinates or
+    # exchanged operand layouts (an out-of-range index or a shape error counts
+    # as failing); on the pair where the two layouts differ
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _check_points(mutant, "k", "mn")

@@ -17,9 +17,8 @@ from tests.gpu_util import compare_full, compare_sampled, new_handle, run_gpu, s
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = ["256x256x64_w4_s2", "256x128x64_w4_s3", "128x128x64_w4_s4", "32x256x64_w4_s4",
-           "128x128x64_w4_s4_kmask", "256x256x64_w8_pingpong",
-           "256x256x64_w8_pp2", "128x128x64_w4_s2", "32x128x64_w4_s6"]
+CONFIGS = ["128x128x64_w4_s4", "128x128x64_w4_s4_kmask", "256x256x64_w8_pp2",
+           "128x128x64_w4_s2", "32x128x64_w4_s6"]
 
 
 @pytest.fixture(scope="module")
@@ -95,7 +94,7 @@ def test_small_integers_bitwise(config, splits):
     hh.close()
 
 
-@pytest.mark.parametrize("config", ["256x256x64_w8_pp2", "256x256x64_w8_pingpong"])
+@pytest.mark.parametrize("config", ["256x256x64_w8_pp2", "128x128x64_w4_s4"])
 @pytest.mark.parametrize("K", [8, 64, 128, 192, 200])
 def test_short_k_bitwise(config, K):
     # one to four k-slabs: the prologue and drain paths of the multi-slab rings
@@ -166,7 +165,9 @@ def test_rank1_whole_output_at_full_size(M, N, K):
 
 # ------------------------------------------------------------ the workloads at full size
 
-WORKLOADS = [
+# Shapes the oracle finishes in a few seconds on the host (60-70 G multiply-adds
+# at most): compared with the oracle on every output element.
+WORKLOADS_FULL = [
     # M, N, K, in, out, dist
     (4096, 4096, 4096, "bf16", "bf16", "uniform"),
     (4096, 4096, 4096, "fp16", "bf16", "uniform"),
@@ -175,19 +176,38 @@ WORKLOADS = [
     (256, 8192, 28672, "bf16", "bf16", "llm"),
     (256, 10240, 8192, "bf16", "bf16", "llm"),
     (256, 8192, 8192, "bf16", "bf16", "llm"),
-    (8192, 8192, 8192, "bf16", "bf16", "llm"),
-    (8192, 28672, 8192, "bf16", "bf16", "llm"),
     (127, 28672, 8192, "fp16", "fp32", "uniform"),
     (3000, 3000, 5000, "fp16", "fp32", "uniform"),
+    (1000, 4097, 1536, "fp16", "fp32", "uniform"),
+    (1, 8192, 8192, "fp16", "fp32", "uniform"),
+]
+
+# The two prefill shapes (550 and 1924 G multiply-adds): whole rows and random
+# points against the oracle.
+WORKLOADS_SAMPLED = [
+    (8192, 8192, 8192, "bf16", "bf16", "llm"),
+    (8192, 28672, 8192, "bf16", "bf16", "llm"),
 ]
 
 
-@pytest.mark.parametrize("M,N,K,ind,outd,dist", WORKLOADS)
-def test_workloads_sampled(h, M, N, K, ind, outd, dist):
-    say("case workload M=%d N=%d K=%d %s->%s %s" % (M, N, K, ind, outd, dist))
+@pytest.mark.parametrize("M,N,K,ind,outd,dist", WORKLOADS_FULL)
+def test_workloads_every_element(h, M, N, K, ind, outd, dist):
+    say("case workload (every element) M=%d N=%d K=%d %s->%s %s" % (M, N, K, ind, outd, dist))
     A, B = make_operands(M, N, K, ind, dist, seed=0)
     C = run_gpu(h, A, B, K, ind, outd)
-    err, worst = compare_sampled(C, A, B, K, ind, outd, "M=%d N=%d K=%d" % (M, N, K))
+    err, worst = compare_full(C, A, B, K, ind, outd, "M=%d N=%d K=%d" % (M, N, K))
+    say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
+    del C
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M,N,K,ind,outd,dist", WORKLOADS_SAMPLED)
+def test_workloads_sampled(h, M, N, K, ind, outd, dist):
+    say("case workload (sampled) M=%d N=%d K=%d %s->%s %s" % (M, N, K, ind, outd, dist))
+    A, B = make_operands(M, N, K, ind, dist, seed=0)
+    C = run_gpu(h, A, B, K, ind, outd)
+    err, worst = compare_sampled(C, A, B, K, ind, outd, "M=%d N=%d K=%d" % (M, N, K),
+                                 n_rows=8, n_points=20000)
     say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
     torch.cuda.empty_cache()
 
