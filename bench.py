@@ -299,13 +299,6 @@ def time_config(g, cfg, iters=50, warmup=10, check=True):
     import torch
     from gemm_inputs import make_operands
     from dense_gemm_nt_amd import roofline
-
-    if args.all_configs:
-        for cfg in CONFIGS:
-            if args.config and cfg[0] not in args.config:
-                continue
-            print(json.dumps(time_config(g, cfg, check=not args.no_check)), flush=True)
-        return
     name, M, N, K, in_dt, out_dt, dist, sets = cfg
     dev = torch.device("cuda", 0)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
@@ -467,6 +460,13 @@ def main():
         sys.exit(1)
 
     from dense_gemm_nt_amd import roofline
+
+    if args.all_configs:
+        for cfg in CONFIGS:
+            if args.config and cfg[0] not in args.config:
+                continue
+            print(json.dumps(time_config(g, cfg, check=not args.no_check)), flush=True)
+        return
 
     # primary: 4096^3 bf16 -> bf16, six rotating input sets (6 x 96 MB > 256 MB cache)
     shapes = (4096, 4096, 4096)

@@ -17,9 +17,9 @@ SOURCES = [os.path.join(CSRC, f) for f in (
     "gemm_nt.hip", "launch_tiles_a.hip", "launch_tiles_b.hip",
     "launch_pp2.hip", "launch_pp2_km.hip", "launch_pp2_mk.hip", "launch_pp2_mm.hip",
     "launch_pp2_f8_e4e4.hip", "launch_pp2_f8_e4e5.hip", "launch_pp2_f8_e5e4.hip",
-    "launch_pp2_f8_e5e5.hip", "launch_pp2_grouped.hip", "launch_pp2_persistent.hip")]
+    "launch_pp2_f8_e5e5.hip", "launch_pp2_grouped.hip", "launch_pp2_persistent.hip", "launch_w4.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp",
-                                           "gemm_nt_pp2.hpp",
+                                           "gemm_nt_pp2.hpp", "gemm_nt_w4.hpp",
                                            "gemm_nt_launch.hpp", "launch_pp2.hip",
                                            "launch_pp2_f8.hip", "launch_tiles_a.hip")] + \
     [os.path.join(ROOT, "include", "gemm_nt.h")]

@@ -22,6 +22,7 @@
 #include "gemm_nt.h"
 #include "gemm_nt_launch.hpp"
 
+
 namespace {
 
 using gnt::KernelArgs;
@@ -81,6 +82,7 @@ const Config kConfigs[] = {
     {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk},
     {"128x128x64_w4_s2", 128, 128, 64, 4, 2, 65536, 0, 1, gnt::kTile128x128_w4_s2},
     {"32x128x64_w4_s6", 32, 128, 64, 4, 6, 122880, 0, 1, gnt::kTile32x128_w4_s6},
+    {"256x256x64_w4_u5", 256, 256, 64, 4, 5, 163840, 0, 1, gnt::kW4},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
@@ -89,6 +91,7 @@ enum {
     CFG_PP2_256x256 = 2,
     CFG_W4_128x128_S2 = 3,
     CFG_W4_32x128 = 4,
+    CFG_W4_256x256 = 5,
 };
 
 struct Plan {
@@ -180,11 +183,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         splits = 1;
     } else if (force_splits > 0) {
         splits = force_splits;
-    } else if (tiles < kNumCUs && p.k_tiles >= 16) {
-        // Fill the compute units, keeping at least 8 k-slabs per split (20 for
-        // the 256x256 tile, whose 256 KB FP32 partial per split costs as much
-        // as streaming about 4 slabs of B).
-        const int min_slabs = cfg == CFG_PP2_256x256 ? 20 : 8;
+    } else if (tiles < kNumCUs && (int64_t)p.k_tiles * c.bk >= 16 * 64) {
+        // Fill the compute units, keeping at least 512 of K per split (1280
+        // for the 256x256 tiles, whose 256 KB FP32 partial per split costs as
+        // much as streaming about 256 of K of B).
+        const int min_slabs = (c.bm == 256 ? 20 : 8) * 64 / c.bk;
         splits = (int)(kNumCUs / tiles);
         if (splits > p.k_tiles / min_slabs)
             splits = p.k_tiles / min_slabs;
@@ -471,14 +474,23 @@ gemm_status_t check_device(gemm_handle_t h)
     return dev == h->device ? GEMM_OK : GEMM_ERR_INVALID_ARG;
 }
 
+// Device memory for split-K and stream-K partials (the handle's workspace).
+struct Workspace {
+    float *partials;
+    int64_t bytes;
+    int log;
+};
+
+Workspace workspace_of(gemm_handle_t h) { return Workspace{h->partials, h->ws_bytes, h->log}; }
+
 // Fill the plan-, output- and epilogue-dependent fields of `a` (whose operand
 // fields the caller has set), then enqueue the kernel and, with split-K, the
 // ordered sum of the partials.
-gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn fn, void *C,
+gemm_status_t enqueue(const Workspace &ws, const Plan &p, KernelArgs &a, launch_fn fn, void *C,
                       int64_t M, int64_t N, int64_t K, int64_t ldc, int out_dtype,
                       const gemm_epilogue_t *epi, hipStream_t stream)
 {
-    if ((p.splits > 1 || p.stream) && p.ws_bytes > h->ws_bytes)
+    if ((p.splits > 1 || p.stream) && p.ws_bytes > ws.bytes)
         return GEMM_ERR_UNSUPPORTED;
     if (p.grid <= 0 || p.grid >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
@@ -499,7 +511,7 @@ gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn f
     a.rows16 = ((ldc * out_size) % 16 == 0) && ((uintptr_t)C % 16 == 0);
     // B, when at most two tile rows of blocks read it, is streamed
     a.nt_b = p.tiles_m <= 2;
-    a.partials = h->partials;
+    a.partials = ws.partials;
     a.sk_units = p.stream ? (int)p.sk_units : 0;
     a.sk_maxseg = p.sk_maxseg;
     a.alpha = 1.0f;
@@ -513,7 +525,7 @@ gemm_status_t enqueue(gemm_handle_t h, const Plan &p, KernelArgs &a, launch_fn f
         a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && a.bias_along == GEMM_BIAS_NONE &&
                   a.act == GEMM_ACT_NONE);
     }
-    if (h->log)
+    if (ws.log)
         fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld%s\n",
                 (long long)M, (long long)N, (long long)K, kConfigs[p.cfg].name, p.tiles_m,
                 p.tiles_n, p.splits, p.kt_per_split, (long long)p.grid, p.stream ? " stream-K" : "");
@@ -572,7 +584,7 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
         fn = gnt::kPP2_persistent[in_dtype][out_dtype];
         q.grid = kNumCUs;
     }
-    return enqueue(h, q, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
+    return enqueue(workspace_of(h), q, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
 }
 
 }  // extern "C"
@@ -883,7 +895,7 @@ gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void
     static LaunchTableRef const kF8[2][2] = {{gnt::kPP2_f8_e4e4, gnt::kPP2_f8_e4e5},
                                              {gnt::kPP2_f8_e5e4, gnt::kPP2_f8_e5e5}};
     const launch_fn fn = kF8[a_dtype == GEMM_FP8_E5M2][b_dtype == GEMM_FP8_E5M2][scales->mode][out_dtype];
-    return enqueue(h, p, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
+    return enqueue(workspace_of(h), p, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
 }
 
 }  // extern "C"

@@ -176,14 +176,19 @@ __device__ __forceinline__ f32x16 mfma32x32x64_f8(u32x4 b0, u32x4 b1, u32x4 a0, 
 }
 
 // Swizzle key of LDS row r for a row of CH 16-byte chunks.  Depends only on
-// r mod 16, so every 32-row MFMA operand block sees the same pattern.
+// r mod 16, so every 16-row group a load fills and every 32-row MFMA operand
+// block sees the same pattern.  Sixteen consecutive rows reading one logical
+// chunk land in sixteen different groups of four banks (of 64): for 128-byte
+// rows through the low three row bits and the row's half of the bank array,
+// for 64-byte rows through r mod 4 (which quarter of the banks the row starts
+// in) and (r / 4) mod 4.
 template <int CH>
 __device__ __forceinline__ int row_key(int r)
 {
     if constexpr (CH == 8)
         return (r & 7) ^ ((r >> 3) & 1);
     else
-        return ((r >> 1) ^ (r >> 3)) & 3;
+        return (r >> 2) & 3;
 }
 
 // Launch-order position of block `bid` among G blocks: the hardware deals

@@ -1,0 +1,360 @@
+// gemm_nt_w4.hpp -- four-wave 256x256 NT GEMM tile for gfx950: one wave per
+// SIMD, each wave owning a 128 x 128 block of C whose FP32 accumulators fill
+// the accumulation registers, over an LDS ring of five 32 KB units.
+//
+// Why this shape.  A 32x32x16 MFMA step of a wave with a WM x WN block reads
+// (WM + WN) / 32 operand fragments of 1 KB from LDS for WM WN / 1024 MFMAs.  At
+// 128 x 128 that is 8 fragment reads per 16 MFMAs; at 64 x 128 (the eight-wave
+// ping-pong tile) 6 per 8.  One third less LDS read traffic per MFMA leaves
+// the LDS with headroom under the matrix cores and spends less energy per
+// FLOP on a part whose clock the power limit sets.  A wave needs 256 FP32
+// accumulators per lane for that block, which only one wave per SIMD has room
+// for (512 registers per lane); so the wave itself overlaps everything: its
+// MFMAs run while it issues the fragment reads of the next k-step and the
+// direct-to-LDS loads of later slabs ("A Blackwell GEMM by Hand in CuTe DSL",
+// section 3: the copies of later stages overlap the MMAs of the current one;
+// "Matmul on sm_120", kernel 3: the shared-memory and register pipelines
+// nested).
+//
+// Ring.  A slab is 64 deep: 256 rows of 128 bytes per operand, one 32 KB unit
+// each.  Every load instruction fetches whole 128-byte rows (8 rows per 1 KB
+// wave-wide load), so each request is one cache line.  The 160 KB of LDS hold
+// five units: A(i) lives in unit i mod 2, B(i) in unit 2 + i mod 3.  The
+// barrier of slab i frees both of its units; A(i + 2) and B(i + 3) go into
+// them.  So B, the operand a decode-shaped call streams from HBM, is issued
+// about five k-steps before the barrier that needs it, and A about three
+// (section 7: enough stages in flight for the load latency).  Logical 16-byte
+// chunk c of row r sits at physical chunk c ^ key(r) (section 6: the XOR
+// swizzle; row_key), and the direct-to-LDS load, which writes 1 KB
+// lane-contiguously, applies it on the global side: the lane that fills
+// physical chunk p of row r fetches logical chunk p ^ key(r).
+//
+// Hand-off (sections 2-3: full/empty barriers).  One workgroup barrier per
+// slab, before its last k-step: every wave then holds the slab's last
+// fragments in registers (the slab's units may be refilled) and has seen its
+// own loads of the next slab land (vmcnt); after it, the next slab's first
+// fragments are read under the last k-step's MFMAs.  Each k-step issues four
+// of a wave's sixteen loads per slab beside its MFMAs, so the four waves'
+// vector-memory issue is spread over the slab.
+//
+// Output: wave w owns rows [128 (w / 2), +128) and columns [128 (w % 2), +128)
+// as 4 x 4 blocks of 32 x 32.  The B fragment is the MFMA's first operand, so
+// accumulator register 4q + e of lane l in block (fn, fm) holds
+// C[32 fm + l % 32][32 fn + 8 q + 4 (l / 32) + e].  Requires K % 8 == 0.
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_nt_common.hpp"
+
+namespace gnt {
+
+// One wave's 128 x 128 block of C (or of a split-K partial) stored through its
+// own 32 KB of LDS so that each store instruction writes whole row segments
+// ("Optimizing GEMMs using tcgen05 - Part 1": the staged store that replaced
+// scattered stores).  Rows are staged as T values (32 or 64 rows... per pass:
+// 128 rows of 16-bit values, 64 rows of FP32), the 16-byte chunk c of staged
+// row r at chunk c ^ (r mod 16), so the column-wise writes of the accumulator
+// layout spread over the banks.  The read-back gives each lane a 16-byte
+// piece of a row.  NT stores with the non-temporal policy.  `dst` is the
+// block's first element, in rows of `ld` elements.
+template <typename T, bool NT = false>
+__device__ __forceinline__ void store_wave_block_staged(const f32x16 (&acc)[4][4], uint8_t *stage, T *dst,
+                                                        int64_t ld, int lane)
+{
+    constexpr int ES = sizeof(T);
+    constexpr int ROWB = 128 * ES;           // staged row bytes (256 or 512)
+    constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+    constexpr int ROWS = 32768 / ROWB;       // rows per pass (128 or 64)
+    constexpr int PASSES = 128 / ROWS;
+    const int h = lane >> 5, r0 = lane & 31;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+#pragma unroll
+        for (int fmp = 0; fmp < ROWS / 32; ++fmp) {
+            const int fm = pass * (ROWS / 32) + fmp;
+            const int r = fmp * 32 + r0;
+#pragma unroll
+            for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int byte = (fn * 32 + 8 * q + 4 * h) * ES;
+                    const int c = (byte >> 4) ^ (r & 15);
+                    uint8_t *a = stage + r * ROWB + c * 16 + (byte & 15);
+                    if constexpr (ES == 4) {
+                        const f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                         acc[fn][fm][4 * q + 3]};
+                        *reinterpret_cast<f32x4 *>(a) = v;
+                    } else {
+                        uint16_t e[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (__is_same(T, __bf16))
+                                e[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[fn][fm][4 * q + i]));
+                            else
+                                e[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[fn][fm][4 * q + i]));
+                        }
+                        const u32x2 w = {(uint32_t)e[0] | ((uint32_t)e[1] << 16),
+                                         (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+                        *reinterpret_cast<u32x2 *>(a) = w;
+                    }
+                }
+        }
+        wait_lgkmcnt0();
+        constexpr int RPR = 64 / CPR;        // rows per read instruction
+#pragma unroll
+        for (int j = 0; j < ROWS / RPR; ++j) {
+            const int r = j * RPR + lane / CPR;
+            const int c = lane % CPR;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * ROWB + ((c ^ (r & 15)) * 16));
+            T *g = dst + (int64_t)(pass * ROWS + r) * ld + c * (16 / ES);
+            if constexpr (NT)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(g));
+            else
+                *reinterpret_cast<u32x4 *>(g) = v;
+        }
+        wait_lgkmcnt0();
+    }
+}
+
+// Every other store of a wave's 128 x 128 block: ragged edges, the fused
+// epilogue, split-K partials.  The FP32 accumulators go through the wave's 32 KB
+// of LDS in two passes of 64 rows (512-byte rows, chunk c of row r at c ^ (r mod
+// 16)); read back, each lane holds four consecutive columns of one row, to
+// which the epilogue is applied (the bias and prior-C reads are then
+// row-contiguous) before a predicated store.  Rows at or past M and columns at
+// or past N are not stored.  The block's first element is C[r0][c0].
+template <int OUT>
+__device__ __forceinline__ void store_wave_block_any(const KernelArgs &p, const f32x16 (&acc)[4][4],
+                                                     uint8_t *stage, int r0, int c0, int split, int lane)
+{
+    constexpr int ROWB = 512;
+    const int h = lane >> 5, rl = lane & 31;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int fmp = 0; fmp < 2; ++fmp) {
+            const int fm = 2 * pass + fmp;
+            const int r = fmp * 32 + rl;
+#pragma unroll
+            for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = (fn * 8 + 2 * q + h) ^ (r & 15);
+                    const f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                     acc[fn][fm][4 * q + 3]};
+                    *reinterpret_cast<f32x4 *>(stage + r * ROWB + c * 16) = v;
+                }
+        }
+        wait_lgkmcnt0();
+#pragma unroll 2
+        for (int it = 0; it < 32; ++it) {
+            const int r = 2 * it + (lane >> 5), c = lane & 31;
+            const int m = r0 + 64 * pass + r, n = c0 + 4 * c;
+            if (m < p.M && n < p.N) {
+                f32x4 x = *reinterpret_cast<const f32x4 *>(stage + r * ROWB + ((c ^ (r & 15)) * 16));
+                store_result<OUT>(p, split, m, n, x);
+            }
+        }
+        wait_lgkmcnt0();
+    }
+}
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
+{
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int PITCH = 128;                // bytes per LDS row (64 16-bit values)
+    constexpr int CH = 8;                     // 16-byte chunks per row
+    constexpr int UNIT = 256 * PITCH;         // one operand of one slab, 32 KB
+    constexpr int UNITS = 5;                  // A: units 0, 1; B: units 2, 3, 4
+    constexpr int FM = 4, FN = 4;
+    static_assert(UNITS * UNIT <= 160 * 1024, "LDS budget");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[UNITS * UNIT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn, split;
+    map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kt0 = split * p.kt_per_split;
+    const int nk = min(p.k_tiles, kt0 + p.kt_per_split) - kt0;
+
+    const int rows_a = min(BM, p.M - m0);
+    const int rows_b = min(BN, p.N - n0);
+    const __amdgpu_buffer_rsrc_t rsA =
+        make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)rows_a * (uint32_t)p.lda * 2u);
+    const __amdgpu_buffer_rsrc_t rsB =
+        make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)rows_b * (uint32_t)p.ldb * 2u);
+
+    // Load j (0..7) of wave w for one operand covers tile rows 32 j + 8 w + lane / 8:
+    // lane l fills physical chunk l % 8 of its row, which holds logical chunk
+    // (l % 8) ^ key(row).  The row step 32 keeps the row mod 16, hence the key,
+    // the same for every load of the wave.
+    const int lr = lane >> 3;
+    const int lc = (lane & 7) ^ row_key<CH>(8 * wave + lr);
+    const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+    const uint32_t voffA = (uint32_t)lr * lda2 + (uint32_t)lc * 16u;
+    const uint32_t voffB = (uint32_t)lr * ldb2 + (uint32_t)lc * 16u;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // Load j of operand `op` (0: A, 1: B) of local slab i into unit u.  Rows
+    // past the tile's valid rows and chunks at or past K read zeros.  So does a
+    // slab at or past nk: the main loop issues the loads of later slabs on
+    // every step, and past the last slab they fill a unit no later slab reads
+    // with zeros (an out-of-range offset touches no memory), which keeps every
+    // wait count of the loop the same.
+    auto issue_one = [&](int op, int i, int u, int j, auto nt) {
+        const int kt = kt0 + i;
+        const bool kin = i < nk && lc * 8 < p.K - kt * BK;
+        const uint32_t kb = (uint32_t)kt * (uint32_t)(BK * 2);
+        const int row = 32 * j + 8 * wave;
+        const uint32_t dst = lds0 + (uint32_t)(u * UNIT + row * PITCH);
+        if (op == 0) {
+            const uint32_t v = (kin && row + lr < rows_a) ? voffA : kOutOfRange;
+            load_lds16(rsA, v, kb + (uint32_t)row * lda2, dst);
+        } else {
+            const uint32_t v = (kin && row + lr < rows_b) ? voffB : kOutOfRange;
+            load_lds16_policy<decltype(nt)::value>(rsB, v, kb + (uint32_t)row * ldb2, dst);
+        }
+    };
+
+    // Fragment read ks (0..3) of a slab: lane l reads row l % 32 of each 32-row
+    // block, k 16 ks + 8 (l / 32) .. +8, i.e. logical chunk 2 ks + l / 32.
+    const int fr = lane & 31;
+    const int roff0 = fr * PITCH + ((lane >> 5) ^ row_key<CH>(fr)) * 16;
+    u32x4 fa[2][FM], fb[2][FN];
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+
+    // Fragment read n (0..7) of k-step ks from units (ua, ub) into buffer `buf`,
+    // in the order the MFMAs below consume them: B block 0, A blocks 0..3, B
+    // blocks 1..3.
+    auto read_one = [&](int ua, int ub, int ks, int buf, int n) {
+        const int off = roff0 ^ (32 * ks);
+        if (n >= 1 && n <= 4)
+            fa[buf][n - 1] =
+                *reinterpret_cast<const u32x4 *>(smem + ua * UNIT + off + (wm * 128 + (n - 1) * 32) * PITCH);
+        else {
+            const int f = n == 0 ? 0 : n - 4;
+            fb[buf][f] = *reinterpret_cast<const u32x4 *>(smem + ub * UNIT + off + (wn * 128 + f * 32) * PITCH);
+        }
+    };
+    // MFMA t (0..15) of a k-step on buffer `buf`: B block t / 4 against A block t % 4.
+    auto mfma_one = [&](int buf, int t) {
+        acc[t >> 2][t & 3] = mfma32x32x16<IN>(fb[buf][t >> 2], fa[buf][t & 3], acc[t >> 2][t & 3]);
+    };
+
+    // The main loop for one B load policy (a compile-time flag: the policy is
+    // an immediate of the load instruction).  Its body has no branch, so the
+    // compiler keeps every accumulator in place across it, and its order is
+    // fixed by scheduling barriers: within each k-step the eight fragment
+    // reads of the next k-step go out beside the first eight MFMAs and four
+    // loads beside MFMAs 2, 5, 8 and 11; the slab's barrier comes before the
+    // last two MFMAs of k-step 2, which keep the matrix core busy while the
+    // waves meet.
+    auto main_loop = [&](auto nt) {
+        // Prologue: A(0), B(0), B(1) and the first half of A(1); then slab 0
+        // landed (12 loads of this wave may still be in flight).
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            issue_one(0, 0, 0, j, nt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            issue_one(1, 0, 2, j, nt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            issue_one(1, 1, 3, j, nt);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            issue_one(0, 1, 1, j, nt);
+        wait_vmcnt<12>();
+        wg_barrier();
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+            read_one(0, 2, 0, 0, n);
+
+        // One k-step: MFMAs t0..t1-1 on buffer mbuf, with read t (t < 8) of
+        // k-step rks from units (rua, rub) into rbuf and load t / 3 (t = 2, 5,
+        // 8, 11) of `load`.
+        auto kstep = [&](int mbuf, int rua, int rub, int rks, int rbuf, auto load, int t0, int t1) {
+#pragma unroll
+            for (int t = t0; t < t1; ++t) {
+                mfma_one(mbuf, t);
+                if (t < 8)
+                    read_one(rua, rub, rks, rbuf, t);
+                if (t % 3 == 2 && t <= 11)
+                    load(t / 3);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        int ua = 0, ub = 2;                                 // units of slab i
+        for (int i = 0; i < nk; ++i) {
+            const int ua1 = ua ^ 1;                         // A(i + 1), A(i - 1)
+            const int ub1 = ub == 4 ? 2 : ub + 1;           // B(i + 1)
+            const int ub2 = ub == 2 ? 4 : ub - 1;           // B(i + 2) = B(i - 1)
+            // k-step 0: the second half of A(i + 1)
+            kstep(0, ua, ub, 1, 1, [&](int j) { issue_one(0, i + 1, ua1, 4 + j, nt); }, 0, 16);
+            // k-steps 1, 2: B(i + 2)
+            kstep(1, ua, ub, 2, 0, [&](int j) { issue_one(1, i + 2, ub2, j, nt); }, 0, 16);
+            auto load_b2 = [&](int j) { issue_one(1, i + 2, ub2, 4 + j, nt); };
+            kstep(0, ua, ub, 3, 1, load_b2, 0, 14);
+            // every wave holds this slab's last fragments and has its own loads
+            // of slab i + 1 landed (B(i + 2) may be in flight); the barrier
+            // publishes both
+            wait_lgkmcnt0();
+            wait_vmcnt<8>();
+            wg_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(0, ua, ub, 3, 1, load_b2, 14, 16);
+            // k-step 3: the first fragments of slab i + 1, and the first half of
+            // A(i + 2) into the unit A(i) has left
+            kstep(1, ua1, ub1, 0, 0, [&](int j) { issue_one(0, i + 2, ua, j, nt); }, 0, 16);
+            ua = ua1;
+            ub = ub1;
+        }
+    };
+
+    if (nk > 0) {
+        if (p.nt_b)
+            main_loop(std::true_type{});
+        else
+            main_loop(std::false_type{});
+    }
+
+    // Epilogue.  Every wave is past its last fragment read and every load has
+    // landed; after the barrier the ring is free for staging (32 KB per wave).
+    const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+    const int r0 = m0 + wm * 128, c0 = n0 + wn * 128;
+    uint8_t *stage = smem + wave * 32768;
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (full && p.splits == 1 && p.rows16 && !p.epi) {
+        if constexpr (OUT == OUT_BF16)
+            store_wave_block_staged<__bf16, true>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)r0 * p.ldc + c0,
+                                                  p.ldc, lane);
+        else if constexpr (OUT == OUT_FP16)
+            store_wave_block_staged<_Float16, true>(acc, stage,
+                                                    static_cast<_Float16 *>(p.C) + (int64_t)r0 * p.ldc + c0, p.ldc,
+                                                    lane);
+        else
+            store_wave_block_staged<float, true>(acc, stage, static_cast<float *>(p.C) + (int64_t)r0 * p.ldc + c0,
+                                                 p.ldc, lane);
+    } else {
+        store_wave_block_any<OUT>(p, acc, stage, r0, c0, split, lane);
+    }
+}
+
+}  // namespace gnt

@@ -1,73 +1,98 @@
-"""Bank model of the LDS tile layout the GEMM kernel uses (host-side, no GPU).
+"""Bank model of the LDS layouts the kernels use (host side, no GPU).
 
-Model (from "A Blackwell GEMM by Hand in CuTe DSL: TMA, mbarriers, TMEM, and
-tcgen05", section 6, The swizzle): memory is split into banks of 4-byte words;
-a group of lanes is served in one pass when no bank has to deliver two different
-words; the cost of a group is the largest number of distinct words one bank must
-deliver.  A 128-byte XOR swizzle permutes the eight 16-byte chunks of a 128-byte
-row by the row index, so the same logical chunk of consecutive rows lands in
-different banks.  The page's own table (32 banks, 8 rows of 16 bytes) pins
-`passes` and `sw128` here.
+"A Blackwell GEMM by Hand in CuTe DSL: TMA, mbarriers, TMEM, and tcgen05",
+section 6 (The swizzle), describes shared memory as banks of 4-byte words: the
+lanes served together cost one pass per distinct word the busiest bank must
+deliver (the same word for several lanes is a broadcast).  Its XOR swizzle moves
+the 16-byte chunks of a 128-byte row by the row index modulo 8, so one logical
+chunk column of eight rows lands in eight different bank groups.  The page
+prints the pass counts and the chunk permutation for that example; the tests
+reproduce them with `group_passes` and `page_swizzle`.
 
-The kernel stores every operand tile K-major, one 128-byte row (64 16-bit values)
-per M or N index, and puts logical chunk c of row r at physical chunk
-c ^ key(r).  `KEY_MODES` lists the keys the kernel can be built with; the tests
-show which of them give one pass per group for both 32-bank / 8-lane and
-64-bank / 16-lane groupings of the MFMA operand read (64 lanes, lane l reads row
-l % 32, chunk 2*ks + l // 32).
+The kernels store each operand K-major, one LDS row per M or N index, and put
+logical chunk c of row r at physical chunk c ^ key(r) (`ROW_KEYS`, by row
+length).  Both keys depend on r mod 16 only: a direct-to-LDS load fills 16
+rows (64-byte rows) or 8 rows (128-byte rows) with one fixed lane-to-chunk map,
+and an MFMA operand read covers 32 rows, so any dependence on a higher row bit
+would make the loading lane and the reading lane disagree about where a chunk
+lives.  The tests check that, that the loads' lane-to-chunk map is a
+permutation of each row, and the pass counts of the MFMA operand read (lane l
+reads row l % 32 of a 32-row block, logical chunk 2 ks + l // 32) for 16 lanes
+over 64 banks and 8 lanes over 32 banks.
 """
 from __future__ import annotations
 
+from collections import defaultdict
 
-def sw128(addr: int) -> int:
-    """XOR address bits 7..9 (row within an 8-row period) into bits 4..6 (16-byte chunk)."""
-    return addr ^ (((addr >> 7) & 0b111) << 4)
+WORD = 4        # bytes per bank word
+CHUNK = 16      # bytes per lane of a 128-bit access
 
 
-def passes(addrs, banks=32, word_bytes=4, access_bytes=16) -> int:
-    """Largest number of distinct words any bank must serve for these accesses."""
-    per_bank = {}
+def group_passes(addrs, banks=32, access=CHUNK) -> int:
+    """Passes one group of lanes needs: each lane reads `access` bytes from its
+    byte address; a bank delivers one word per pass."""
+    wanted = defaultdict(set)                # bank -> distinct words asked of it
     for a in addrs:
-        for w in range(access_bytes // word_bytes):
-            word = a // word_bytes + w
-            per_bank.setdefault(word % banks, set()).add(word)
-    return max(len(s) for s in per_bank.values()) if per_bank else 0
+        first = a // WORD
+        for w in range(first, first + access // WORD):
+            wanted[w % banks].add(w)
+    return max((len(v) for v in wanted.values()), default=0)
 
 
-# Row keys the kernel can use; the number is its template argument.
-KEY_MODES = {
-    0: lambda r: r & 7,                 # the 128-byte swizzle of the page
-    1: lambda r: (r ^ (r >> 3)) & 7,    # also separates rows r and r+8
-    2: lambda r: (r >> 1) & 7,          # pairs of rows share a key
+def page_swizzle(addr: int) -> int:
+    """The page's 128-byte swizzle: the chunk index inside a 128-byte row is
+    XORed with the row index modulo 8 (bytes inside a chunk stay put)."""
+    row, in_row = divmod(addr, 128)
+    chunk, byte = divmod(in_row, CHUNK)
+    return row * 128 + CHUNK * (chunk ^ (row % 8)) + byte
+
+
+# The kernels' keys, by LDS row length in bytes (gemm_nt_common.hpp, row_key).
+ROW_KEYS = {
+    128: lambda r: (r & 7) ^ ((r >> 3) & 1),   # eight chunks; r and r + 8 differ too
+    64: lambda r: (r >> 2) & 3,                # four chunks; (r / 4) mod 4
 }
 
 
-def kernel_offset(row: int, chunk: int, mode: int, pitch: int = 128) -> int:
-    """Byte offset of logical 16-byte chunk `chunk` of tile row `row`."""
-    return row * pitch + 16 * (chunk ^ KEY_MODES[mode](row))
+def kernel_offset(row: int, chunk: int, pitch: int = 128, key=None) -> int:
+    """Byte offset of logical chunk `chunk` of row `row` in a kernel tile."""
+    k = ROW_KEYS[pitch] if key is None else key
+    return row * pitch + CHUNK * (chunk ^ k(row))
 
 
-def fragment_read_addrs(ks: int, mode: int, row0: int = 0):
-    """Byte offsets the 64 lanes of one MFMA operand read touch (rows row0..row0+31)."""
-    return [kernel_offset(row0 + (l % 32), 2 * ks + l // 32, mode) for l in range(64)]
+def operand_read(ks: int, row0: int, pitch: int = 128, key=None):
+    """Byte offsets of the 64 lanes of one MFMA operand read: lane l reads row
+    row0 + l % 32, logical chunk 2 ks + l // 32 (8 consecutive 16-bit k values)."""
+    return [kernel_offset(row0 + l % 32, 2 * ks + l // 32, pitch, key) for l in range(64)]
 
 
-def read_passes(mode: int, banks: int, lanes_per_group: int) -> int:
-    """Worst pass count over all lane groups, k-steps and 32-row blocks of a 256-row tile."""
+def worst_read_passes(pitch: int = 128, banks: int = 64, lanes: int = 16, rows: int = 256,
+                      key=None) -> int:
+    """Largest pass count over every lane group, k-step and 32-row block of a
+    `rows`-row tile."""
+    steps = pitch // (2 * CHUNK)
     worst = 0
-    for row0 in range(0, 256, 32):
-        for ks in range(4):
-            addrs = fragment_read_addrs(ks, mode, row0)
-            for g in range(0, 64, lanes_per_group):
-                worst = max(worst, passes(addrs[g:g + lanes_per_group], banks=banks))
+    for row0 in range(0, rows, 32):
+        for ks in range(steps):
+            a = operand_read(ks, row0, pitch, key)
+            for g in range(0, 64, lanes):
+                worst = max(worst, group_passes(a[g:g + lanes], banks))
     return worst
 
 
-def dma_write_is_permutation(mode: int, rows: int = 256) -> bool:
-    """Direct-to-LDS writes land lane-contiguously; each lane fetches the global chunk
-    whose swizzled home is its slot.  True when that map is a bijection per row."""
+def load_map_is_permutation(pitch: int = 128, rows: int = 256, key=None) -> bool:
+    """A direct-to-LDS load writes its lanes' 16-byte pieces contiguously; the
+    lane filling physical chunk p of row r fetches logical chunk p ^ key(r).
+    True when every row's logical chunks land exactly once."""
+    n = pitch // CHUNK
     for r in range(rows):
-        homes = sorted(kernel_offset(r, c, mode) - r * 128 for c in range(8))
-        if homes != [16 * p for p in range(8)]:
+        homes = sorted((kernel_offset(r, c, pitch, key) - r * pitch) // CHUNK for c in range(n))
+        if homes != list(range(n)):
             return False
     return True
+
+
+def key_period_16(pitch: int = 128, key=None) -> bool:
+    """The key depends on the row modulo 16 only."""
+    k = ROW_KEYS[pitch] if key is None else key
+    return all(k(r) == k(r % 16) for r in range(1024))

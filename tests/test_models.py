@@ -58,32 +58,45 @@ def test_bank_model_reproduces_page1_table():
         parts = ln.split()
         if parts[0] == "passes":
             tile_k, pitch, layout, want = int(parts[1]), int(parts[2]), parts[3], parts[4]
-            f = (lambda a: a) if layout == "plain" else lds_model.sw128
-            got = [lds_model.passes([f(r * pitch + c * 16) for r in range(8)])
+            f = (lambda a: a) if layout == "plain" else lds_model.page_swizzle
+            got = [lds_model.group_passes([f(r * pitch + c * 16) for r in range(8)])
                    for c in range(pitch // 16)]
             assert got == [int(x) for x in want.split(",")], ln
         elif parts[0] == "perm":
             r = int(parts[1])
-            got = [(lds_model.sw128(r * 128 + c * 16) - r * 128) // 16 for c in range(8)]
+            got = [(lds_model.page_swizzle(r * 128 + c * 16) - r * 128) // 16 for c in range(8)]
             assert got == [int(x) for x in parts[2].split(",")]
-    # the page's swizzle is key mode 0 of the kernel layout
+    # the kernel's 128-byte key is the page's on rows 0..7
     for r in range(8):
         for c in range(8):
-            assert lds_model.kernel_offset(r, c, 0) == lds_model.sw128(r * 128 + c * 16)
+            assert lds_model.kernel_offset(r, c, 128) == lds_model.page_swizzle(r * 128 + c * 16)
 
 
-@pytest.mark.parametrize("mode", sorted(lds_model.KEY_MODES))
-def test_kernel_layout_is_a_permutation(mode):
-    assert lds_model.dma_write_is_permutation(mode)
+@pytest.mark.parametrize("pitch", [128, 64])
+def test_kernel_layouts_are_permutations_with_period_16(pitch):
+    assert lds_model.load_map_is_permutation(pitch)
+    assert lds_model.key_period_16(pitch)
 
 
-def test_kernel_default_key_is_conflict_free_in_both_bank_models():
-    # key mode 1 serves each MFMA operand read group in one pass whether the LDS
-    # serves 8 lanes over 32 banks or 16 lanes over 64 banks
-    assert lds_model.read_passes(1, banks=32, lanes_per_group=8) == 1
-    assert lds_model.read_passes(1, banks=64, lanes_per_group=16) == 1
-    # the page's key alone conflicts two-way under the 64-bank grouping
-    assert lds_model.read_passes(0, banks=64, lanes_per_group=16) == 2
-    # unswizzled rows serialise fully
-    plain = [l % 32 * 128 for l in range(8)]
-    assert lds_model.passes(plain) == 8
+def test_kernel_keys_serve_each_operand_read_group_in_one_pass():
+    # 128-byte rows: one pass whether 8 lanes are served over 32 banks or 16
+    # lanes over 64 banks; the page's key alone conflicts two-way at 64 banks
+    assert lds_model.worst_read_passes(128, banks=32, lanes=8) == 1
+    assert lds_model.worst_read_passes(128, banks=64, lanes=16) == 1
+    page_key = lambda r: r & 7
+    assert lds_model.worst_read_passes(128, banks=64, lanes=16, key=page_key) == 2
+    # 64-byte rows (the four-wave tile's 32-deep stages): one pass at 64 banks
+    assert lds_model.worst_read_passes(64, banks=64, lanes=16) == 1
+    # unswizzled 64-byte rows: four rows share each bank group
+    assert lds_model.worst_read_passes(64, banks=64, lanes=16, key=lambda r: 0) == 4
+    # unswizzled 128-byte rows serialise fully at 32 banks
+    assert lds_model.group_passes([r * 128 for r in range(8)]) == 8
+
+
+def test_a_key_with_a_higher_row_bit_breaks_the_load_read_agreement():
+    # ((r >> 1) ^ (r >> 3)) & 3 is conflict-free but depends on bit 4 of the
+    # row: a load that computes it from the row within its 16-row group puts
+    # rows 16..31 of each 32-row block where the operand read does not look
+    bad = lambda r: ((r >> 1) ^ (r >> 3)) & 3
+    assert lds_model.worst_read_passes(64, banks=64, lanes=16, key=bad) == 1
+    assert not lds_model.key_period_16(64, key=bad)
