@@ -20,7 +20,7 @@ STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_UNSUPPORTED",
 # Every symbol include/gemm_nt.h declares.
 EXPORTS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_run_layout", "gemm_run_fp8",
            "gemm_run_grouped", "gemm_run_grouped_fp8", "gemm_destroy", "gemm_validate",
-           "gemm_plan", "gemm_status_string")
+           "gemm_plan", "gemm_status_string", "gemm_run_noalloc")
 
 
 class GemmError(RuntimeError):
@@ -92,6 +92,8 @@ def lib():
     L.gemm_destroy.restype = ci
     L.gemm_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci, vp]
     L.gemm_run.restype = ci
+    L.gemm_run_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    L.gemm_run_noalloc.restype = ci
     L.gemm_run_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, ci,
                               ctypes.POINTER(GemmEpilogue), vp]
     L.gemm_run_ex.restype = ci

@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <new>
 #include <vector>
@@ -22,6 +23,13 @@
 #include "gemm_nt.h"
 #include "gemm_nt_launch.hpp"
 
+// Scratch of gemm_run_noalloc: the split-K / stream-K partials of calls that may
+// not allocate.  Each device the library runs on holds its own copy from the
+// first call on it until the process ends.  In host code the name stands for
+// the host-side shadow, never a device address: the device address comes from
+// hipGetSymbolAddress (per device, see noalloc_scratch) and only that address is
+// passed to kernels.
+static __device__ __align__(256) uint8_t scratch[GEMM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -474,7 +482,8 @@ gemm_status_t check_device(gemm_handle_t h)
     return dev == h->device ? GEMM_OK : GEMM_ERR_INVALID_ARG;
 }
 
-// Device memory for split-K and stream-K partials (the handle's workspace).
+// Device memory for split-K and stream-K partials: the handle's workspace, or
+// the static scratch of gemm_run_noalloc.
 struct Workspace {
     float *partials;
     int64_t bytes;
@@ -585,6 +594,67 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
         q.grid = kNumCUs;
     }
     return enqueue(workspace_of(h), q, a, fn, C, M, N, K, ldc, out_dtype, epi, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  Concurrent first calls look it up
+// twice and store the same address.
+gemm_status_t noalloc_scratch(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GEMM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return GEMM_ERR_UNSUPPORTED;
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return GEMM_ERR_HIP;
+        }
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                               int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int in_dtype,
+                               int out_dtype, hipStream_t stream)
+{
+    gemm_status_t st = validate(A, B, C, M, N, K, lda, ldb, ldc, K, K, in_dtype, out_dtype);
+    if (st != GEMM_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    void *ptr = nullptr;
+    if ((st = noalloc_scratch(&ptr)) != GEMM_OK)
+        return st;
+    // gemm_run's plan with its partials bounded by the scratch: K splits or
+    // stream-K that would need more take fewer splits or the split plan
+    const Plan p = make_plan(M, N, K, GEMM_NOALLOC_SCRATCH_BYTES, -1, -1, 1);
+    if ((p.splits > 1 || p.stream) && p.ws_bytes > GEMM_NOALLOC_SCRATCH_BYTES)
+        return GEMM_ERR_UNSUPPORTED;
+    KernelArgs a{};
+    a.A = static_cast<const uint16_t *>(A);
+    a.B = static_cast<const uint16_t *>(B);
+    a.lda = (int)lda;
+    a.ldb = (int)ldb;
+    launch_fn fn = p.stream ? gnt::kPP2_persistent[in_dtype][out_dtype]
+                            : kConfigs[p.cfg].fn[in_dtype][out_dtype];
+    const Workspace ws{static_cast<float *>(ptr), GEMM_NOALLOC_SCRATCH_BYTES, 0};
+    return enqueue(ws, p, a, fn, C, M, N, K, ldc, out_dtype, nullptr, stream);
 }
 
 }  // extern "C"

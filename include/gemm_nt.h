@@ -87,6 +87,29 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C,
                        int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                        int in_dtype, int out_dtype, hipStream_t stream);
 
+/* gemm_run for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  No handle:
+ * split-K and stream-K partials go to a static scratch array of
+ * GEMM_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which the library's code
+ * object holds on each device it runs on from the first call there until the
+ * process ends.  The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).
+ *   Arguments, results and errors as gemm_run on the current device, with one
+ *   difference in the plan: K splits or stream-K whose partials would exceed the
+ *   scratch are planned with fewer splits or without stream-K, so results may
+ *   differ from gemm_run's in the summation order (within the same bound).  A
+ *   plan that still needed more scratch would return GEMM_ERR_UNSUPPORTED with
+ *   nothing enqueued.
+ *   Every call on one device shares that device's scratch: two calls that may
+ *   run concurrently on one device (different streams, or different host
+ *   threads without ordering) race on it.  Serialise them, e.g. on one stream.
+ *   Nothing in the scratch has to start at zero; each call writes every
+ *   partial it reads. */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C,
+                               int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                               int64_t ldc, int in_dtype, int out_dtype, hipStream_t stream);
+
 /* Fused epilogue ("CUTLASS Deep Dive: From CuTe Layouts to Blackwell tcgen05",
  * the Tutorial 01/05 epilogues, "Epilogue Visitor Trees (EVT)" and "Classic
  * Fused Epilogue: Bias + ReLU"): as each output tile is written back,
