@@ -91,6 +91,7 @@ const Config kConfigs[] = {
     {"128x128x64_w4_s2", 128, 128, 64, 4, 2, 65536, 0, 1, gnt::kTile128x128_w4_s2},
     {"32x128x64_w4_s6", 32, 128, 64, 4, 6, 122880, 0, 1, gnt::kTile32x128_w4_s6},
     {"256x256x64_w4_u5", 256, 256, 64, 4, 5, 163840, 0, 1, gnt::kW4},
+    {"256x128x64_w4_u8", 256, 128, 64, 4, 8, 163840, 0, 1, gnt::kW4_128},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
@@ -100,6 +101,7 @@ enum {
     CFG_W4_128x128_S2 = 3,
     CFG_W4_32x128 = 4,
     CFG_W4_256x256 = 5,
+    CFG_W4_256x128 = 6,
 };
 
 struct Plan {

@@ -62,6 +62,10 @@ struct KernelArgs {
     int sk_units;          // stream-K: tiles * k_tiles (0: off); block b of the grid G
                            // takes units [b T / G, (b + 1) T / G) in tile-major order
     int sk_maxseg;         // stream-K: partial slots per block
+    int inreduce;          // split-K reduced in the kernel: partials of tile t, split s
+                           // in slot t * splits + s of `partials` (256 KB each, in
+                           // register order), arrivals counted in counters[t]
+    unsigned *counters;    // per-tile arrival counters, zero between calls
     // fused epilogue D = act(alpha * acc + beta * C_old + bias), applied when epi != 0
     float alpha, beta;
     const float *bias;     // FP32, N values (bias_along == 1) or M values (2)
@@ -224,6 +228,89 @@ __device__ __forceinline__ void map_block(int bid, int G, int tiles_m, int tiles
     const int tiles = tiles_m * tiles_n;
     split = v / tiles;
     tile_order(v - split * tiles, tiles_m, tiles_n, group_m, tm, tn);
+}
+
+// Block id -> (tile row, tile column, K split) with the K splits of one tile
+// adjacent in launch order: they then fall in one XCD's contiguous run of
+// positions (xcd_order), next to each other in its L2, which is where the
+// in-kernel split-K reduction exchanges their partials.
+__device__ __forceinline__ void map_block_split_minor(int bid, int G, int tiles_m, int tiles_n, int group_m,
+                                                      int splits, int &tm, int &tn, int &split)
+{
+    const int v = xcd_order(bid, G);
+    const int t = v / splits;
+    split = v - t * splits;
+    tile_order(t, tiles_m, tiles_n, group_m, tm, tn);
+}
+
+// Split-K reduced inside the GEMM kernel ("A Blackwell GEMM by Hand in CuTe
+// DSL", section 9: split-K for decode, the partials combined by the CTAs
+// themselves instead of a second pass).  Every split of tile t stores its FP32
+// partial, in register order (lane l's register group g of wave w at byte
+// (w * G + g) * 1024 + 16 l of the slot: each store instruction writes 1 KB
+// contiguously), with device-coherent stores, waits for them, and counts its
+// arrival on counters[t].  The split that arrives last adds the other
+// partials to its registers in split order 0, 1, ..., S - 1 (a fixed order:
+// the bits do not depend on which split came last, and equal those of a
+// second pass summing the splits in order), resets the counter for the next
+// call and returns true; the others return false and are done.  No block
+// waits for another, so there is no spin and no dependence on which blocks
+// are resident.  `flag` is a word of LDS no wave is using; every wave of the
+// block calls this with its own accumulators (NW waves, G register groups of
+// four per lane).
+template <int NW, int FN, int FM>
+__device__ __forceinline__ bool splitk_arrive(const KernelArgs &p, f32x16 (&acc)[FN][FM], int tile, int split,
+                                              int wave, int lane, uint32_t *flag)
+{
+    constexpr int G = FN * FM * 4;                        // register groups per lane
+    constexpr uint32_t SLOT = (uint32_t)NW * G * 1024u;   // bytes per split partial
+    const int S = p.splits;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const uint8_t *>(p.partials) + (int64_t)tile * S * SLOT, (uint32_t)S * SLOT);
+    const uint32_t vo = (uint32_t)(wave * G) * 1024u + (uint32_t)lane * 16u;
+    constexpr int SC1 = 16;                               // device-coherent access
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int g = (fn * FM + fm) * 4 + q;
+                const f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                 acc[fn][fm][4 * q + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, vo + g * 1024u,
+                                                       (uint32_t)split * SLOT, SC1);
+            }
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (wave == 0 && lane == 0)
+        *flag = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wg_barrier();
+    const uint32_t arrived = __builtin_amdgcn_readfirstlane(*flag);
+    wg_barrier();                                         // everyone has read the flag
+    if ((int)arrived != S - 1)
+        return false;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int g = (fn * FM + fm) * 4 + q;
+                const f32x4 own = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                   acc[fn][fm][4 * q + 3]};
+                f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int s = 0; s < S; ++s)
+                    sum += s == split ? own
+                                      : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                      rs, vo + g * 1024u, (uint32_t)s * SLOT, SC1));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[fn][fm][4 * q + e] = sum[e];
+            }
+    if (wave == 0 && lane == 0)
+        __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 template <int OUT>

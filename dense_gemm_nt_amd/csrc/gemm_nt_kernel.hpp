@@ -86,15 +86,15 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
 
     // Load j of this wave covers LDS rows (j * NWAVES + wave) * RPI .. +RPI.  A
     // row's swizzle key depends on the row mod 16 only, which is the same for
-    // every j, so this lane's logical chunk lc and its byte offset within the
-    // first row group are fixed; the row step goes into the scalar offset.  Rows
-    // past the tile's last valid row, and chunks at or past K, read as zeros.
+    // every j, so this lane's logical chunk lc is fixed.  Chunks at or past K
+    // read as zeros.  Rows past the tile's last valid row re-read that row
+    // (their outputs are never stored) rather than reading out of range: a load
+    // that touches no memory in any lane may count as done before the loads
+    // issued ahead of it, and the vmcnt waits below count on issue order.
     constexpr int RSTEP = NWAVES * RPI;
     const int lrow0 = wave * RPI + lane / CH;
     const int lc = (lane % CH) ^ row_key<CH>(lrow0);
     const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
-    const uint32_t voffA = (uint32_t)lrow0 * lda2 + (uint32_t)lc * 16u;
-    const uint32_t voffB = (uint32_t)lrow0 * ldb2 + (uint32_t)lc * 16u;
 
     const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
     const uint32_t ldsA = lds_base;
@@ -108,14 +108,15 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
         auto loads = [&](auto nt) {
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j) {
-                const uint32_t v = (kin && lrow0 + j * RSTEP < rows_a) ? voffA : kOutOfRange;
-                load_lds16(rsA, v, koff + (uint32_t)(j * RSTEP) * lda2,
-                           ldsA + s * A_BYTES + (j * NWAVES + wave) * 1024);
+                const uint32_t r = (uint32_t)min(lrow0 + j * RSTEP, rows_a - 1);
+                const uint32_t v = kin ? r * lda2 + (uint32_t)lc * 16u : kOutOfRange;
+                load_lds16(rsA, v, koff, ldsA + s * A_BYTES + (j * NWAVES + wave) * 1024);
             }
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j) {
-                const uint32_t v = (kin && lrow0 + j * RSTEP < rows_b) ? voffB : kOutOfRange;
-                load_lds16_policy<decltype(nt)::value>(rsB, v, koff + (uint32_t)(j * RSTEP) * ldb2,
+                const uint32_t r = (uint32_t)min(lrow0 + j * RSTEP, rows_b - 1);
+                const uint32_t v = kin ? r * ldb2 + (uint32_t)lc * 16u : kOutOfRange;
+                load_lds16_policy<decltype(nt)::value>(rsB, v, koff,
                                                        ldsB + s * B_BYTES + (j * NWAVES + wave) * 1024);
             }
         };

@@ -30,7 +30,7 @@ extern LaunchTable kPP2_f8_e4e4_grouped, kPP2_f8_e4e5_grouped, kPP2_f8_e5e4_grou
 extern LaunchTable kPP2_grouped;
 // persistent blocks over the tiles of one problem (16-bit, K-major)
 extern LaunchTable kPP2_persistent;
-// the four-wave 256x256 tile (gemm_nt_w4.hpp), 16-bit, K-major
-extern LaunchTable kW4;
+// the four-wave 256x256 and 256x128 tiles (gemm_nt_w4.hpp), 16-bit, K-major
+extern LaunchTable kW4, kW4_128;
 
 }  // namespace gnt

@@ -138,8 +138,6 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         const int lrow0 = q * 8 + lane / CH;
         const int lc = (lane % CH) ^ row_key<CH>(lrow0);
         const uint32_t lda2 = (uint32_t)p.lda * ESZ, ldb2 = (uint32_t)p.ldb * ESZ;   // row pitch, bytes
-        const uint32_t voffA = (uint32_t)lrow0 * lda2 + (uint32_t)lc * 16u;
-        const uint32_t voffB = (uint32_t)lrow0 * ldb2 + (uint32_t)lc * 16u;
         const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
         // Load number j (0..3) of the 128-row unit starting at tile row `row0` of
@@ -171,21 +169,24 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     make_rsrc(X + (int64_t)kt * BK * ld + col0,
                               (uint32_t)(((int64_t)rows_left * ld - col0) * 2));
                 const uint32_t ld2 = (uint32_t)ld * 2u;
-                // chunks wholly past column M (N) are not fetched: they would only
-                // feed output rows (columns) that are never stored
-                const int col = row0 + 8 * mn_chunk;
-                const uint32_t v = col < (IS_A ? rows_a : rows_b)
-                                       ? (uint32_t)(4 * q + (lane >> 4)) * ld2 + (uint32_t)col * 2u
-                                       : kOutOfRange;
+                // chunks wholly past column M (N) re-read the last valid chunk:
+                // they only feed output rows (columns) that are never stored
+                const int cmax = ((IS_A ? rows_a : rows_b) - 1) & ~7;
+                const int col = min(row0 + 8 * mn_chunk, cmax);
+                const uint32_t v = (uint32_t)(4 * q + (lane >> 4)) * ld2 + (uint32_t)col * 2u;
                 load_lds16_policy<NT>(rs, v, (uint32_t)(16 * j) * ld2, dst);
             } else {
+                // rows past the tile's valid rows re-read its last valid row
+                // (their outputs are never stored): a load out of range in every
+                // lane touches no memory and may count as done before the loads
+                // issued ahead of it, and the vmcnt waits count on issue order
                 const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * ESZ);
                 const bool kin = lc * 16 < (p.K - kt * BK) * ESZ;
-                const int row = row0 + 32 * j;
                 const int rows = IS_A ? rows_a : rows_b;
                 const uint32_t ld2 = IS_A ? lda2 : ldb2;
-                const uint32_t v = (kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange;
-                load_lds16_policy<NT>(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2, dst);
+                const uint32_t r = (uint32_t)min(lrow0 + row0 + 32 * j, rows - 1);
+                const uint32_t v = kin ? r * ld2 + (uint32_t)lc * 16u : kOutOfRange;
+                load_lds16_policy<NT>(IS_A ? rsA : rsB, v, koff, dst);
             }
         };
         // The eight loads a wave issues in one memory phase, n = 0..7: group 0
@@ -203,16 +204,15 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // Blockwise scales of local slab i (SC == 1).  Group 1 wave q loads the
         // row scales of tile rows 64 q .. +64 (rows of A_0 into the A_0 slot of
         // slab i, rows of A_1 into its A_1 slot); wave 0 of group 0 loads the
-        // scales of the tile's two 128-column blocks of B.  Rows past M and blocks
-        // past N read zeros (their outputs are never stored).
+        // scales of the tile's two 128-column blocks of B.  Rows past M take the
+        // last row's scale and blocks past N read zeros (their outputs are never
+        // stored; lane 0's block is always inside N).
         auto scale_load = [&](auto grp, int i) {
             if constexpr (SC == 1) {
                 const int kt = kt0 + i;
                 if constexpr (decltype(grp)::value == 1) {
-                    const int m = m0 + 64 * q + lane;
-                    const uint32_t v = m < p.M
-                        ? ((uint32_t)(m >> p.sfa_shift) * (uint32_t)p.sf_ld + (uint32_t)kt) * 4u
-                        : kOutOfRange;
+                    const int m = min(m0 + 64 * q + lane, p.M - 1);
+                    const uint32_t v = ((uint32_t)(m >> p.sfa_shift) * (uint32_t)p.sf_ld + (uint32_t)kt) * 4u;
                     const uint32_t dst = q < 2 ? SA0 + (i & 1) * 512 + q * 256
                                                : SA1 + (i % 3) * 512 + (q - 2) * 256;
                     load_lds4(make_rsrc(p.scale_a, p.sfa_bytes), v, 0, lds0 + dst);
@@ -414,12 +414,15 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                 wait_vmcnt<0>();
             } else {
                 issue_loads(G1{}, 0, std::false_type{});
-                if (nk > 1) {
+                if (nk > 1)
                     issue_loads(G1{}, 1, std::false_type{});
+                // An MN-major A slab's k-rows past K are loads out of range in
+                // every lane (they must read zeros) and may count as done early:
+                // no wait counts past the last slab there.
+                if (nk > 2 || (nk == 2 && !AM))
                     wait_vmcnt<A_INFLIGHT>();
-                } else {
+                else
                     wait_vmcnt<0>();
-                }
             }
             phase_end();
             if (group == 0) {
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     memory_phase(G1{}, i, i + 2 < nk, i + 2, std::false_type{}, g1_rows);   // A(i+2)
                     wait_lgkmcnt0();
                     GNT_PP2_EVENT(i, 3);
-                    if (i + 2 < nk)                            // A(i+1) landed
+                    if (i + 3 < nk || (i + 2 < nk && !AM))     // A(i+1) landed
                         wait_vmcnt<A_INFLIGHT>();
                     else
                         wait_vmcnt<0>();

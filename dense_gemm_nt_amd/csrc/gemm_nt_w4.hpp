@@ -49,24 +49,33 @@
 
 namespace gnt {
 
-// One wave's 128 x 128 block of C (or of a split-K partial) stored through its
-// own 32 KB of LDS so that each store instruction writes whole row segments
-// ("Optimizing GEMMs using tcgen05 - Part 1": the staged store that replaced
-// scattered stores).  Rows are staged as T values (32 or 64 rows... per pass:
-// 128 rows of 16-bit values, 64 rows of FP32), the 16-byte chunk c of staged
-// row r at chunk c ^ (r mod 16), so the column-wise writes of the accumulator
-// layout spread over the banks.  The read-back gives each lane a 16-byte
-// piece of a row.  NT stores with the non-temporal policy.  `dst` is the
-// block's first element, in rows of `ld` elements.
-template <typename T, bool NT = false>
-__device__ __forceinline__ void store_wave_block_staged(const f32x16 (&acc)[4][4], uint8_t *stage, T *dst,
+// One wave's 128 x (32 FN) block of C stored through its own 32 KB of LDS so
+// that each store instruction writes whole row segments ("Optimizing GEMMs
+// using tcgen05 - Part 1": the staged store that replaced scattered stores).
+// Rows are staged as T values, as many per pass as 32 KB holds; the 16-byte
+// chunk c of staged row r sits at chunk c ^ key(r), so that the column-wise
+// writes of the accumulator layout spread over the banks.  The read-back gives
+// each lane a 16-byte piece of a row.  NT stores with the non-temporal
+// policy.  `dst` is the block's first element, in rows of `ld` elements.
+template <int CPR>
+__device__ __forceinline__ int stage_key(int r)
+{
+    if constexpr (CPR >= 16)
+        return r & 15;
+    else
+        return row_key<8>(r);
+}
+
+template <typename T, int FN, bool NT = false>
+__device__ __forceinline__ void store_wave_block_staged(const f32x16 (&acc)[FN][4], uint8_t *stage, T *dst,
                                                         int64_t ld, int lane)
 {
     constexpr int ES = sizeof(T);
-    constexpr int ROWB = 128 * ES;           // staged row bytes (256 or 512)
+    constexpr int ROWB = 32 * FN * ES;       // staged row bytes
     constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
-    constexpr int ROWS = 32768 / ROWB;       // rows per pass (128 or 64)
+    constexpr int ROWS = 32768 / ROWB < 128 ? 32768 / ROWB : 128;   // rows per pass
     constexpr int PASSES = 128 / ROWS;
+    static_assert(CPR >= 8, "row of at least 128 bytes");
     const int h = lane >> 5, r0 = lane & 31;
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
@@ -75,11 +84,11 @@ __device__ __forceinline__ void store_wave_block_staged(const f32x16 (&acc)[4][4
             const int fm = pass * (ROWS / 32) + fmp;
             const int r = fmp * 32 + r0;
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int byte = (fn * 32 + 8 * q + 4 * h) * ES;
-                    const int c = (byte >> 4) ^ (r & 15);
+                    const int c = (byte >> 4) ^ stage_key<CPR>(r);
                     uint8_t *a = stage + r * ROWB + c * 16 + (byte & 15);
                     if constexpr (ES == 4) {
                         const f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
@@ -106,7 +115,7 @@ __device__ __forceinline__ void store_wave_block_staged(const f32x16 (&acc)[4][4
         for (int j = 0; j < ROWS / RPR; ++j) {
             const int r = j * RPR + lane / CPR;
             const int c = lane % CPR;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * ROWB + ((c ^ (r & 15)) * 16));
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * ROWB + ((c ^ stage_key<CPR>(r)) * 16));
             T *g = dst + (int64_t)(pass * ROWS + r) * ld + c * (16 / ES);
             if constexpr (NT)
                 __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(g));
@@ -117,27 +126,31 @@ __device__ __forceinline__ void store_wave_block_staged(const f32x16 (&acc)[4][4
     }
 }
 
-// Every other store of a wave's 128 x 128 block: ragged edges, the fused
+// Every other store of a wave's 128 x (32 FN) block: ragged edges, the fused
 // epilogue, split-K partials.  The FP32 accumulators go through the wave's 32 KB
-// of LDS in two passes of 64 rows (512-byte rows, chunk c of row r at c ^ (r mod
-// 16)); read back, each lane holds four consecutive columns of one row, to
-// which the epilogue is applied (the bias and prior-C reads are then
+// of LDS (128 FN-byte rows, as many per pass as fit; chunk c of row r at
+// c ^ (r mod 16)); read back, each lane holds four consecutive columns of one
+// row, to which the epilogue is applied (the bias and prior-C reads are then
 // row-contiguous) before a predicated store.  Rows at or past M and columns at
 // or past N are not stored.  The block's first element is C[r0][c0].
-template <int OUT>
-__device__ __forceinline__ void store_wave_block_any(const KernelArgs &p, const f32x16 (&acc)[4][4],
+template <int OUT, int FN>
+__device__ __forceinline__ void store_wave_block_any(const KernelArgs &p, const f32x16 (&acc)[FN][4],
                                                      uint8_t *stage, int r0, int c0, int split, int lane)
 {
-    constexpr int ROWB = 512;
+    constexpr int ROWB = 128 * FN;           // FP32 row bytes
+    constexpr int CPR = ROWB / 16;
+    constexpr int ROWS = 32768 / ROWB < 128 ? 32768 / ROWB : 128;
+    constexpr int PASSES = 128 / ROWS;
+    constexpr int RPR = 64 / CPR;
     const int h = lane >> 5, rl = lane & 31;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
-        for (int fmp = 0; fmp < 2; ++fmp) {
-            const int fm = 2 * pass + fmp;
+        for (int fmp = 0; fmp < ROWS / 32; ++fmp) {
+            const int fm = pass * (ROWS / 32) + fmp;
             const int r = fmp * 32 + rl;
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c = (fn * 8 + 2 * q + h) ^ (r & 15);
@@ -148,9 +161,9 @@ __device__ __forceinline__ void store_wave_block_any(const KernelArgs &p, const 
         }
         wait_lgkmcnt0();
 #pragma unroll 2
-        for (int it = 0; it < 32; ++it) {
-            const int r = 2 * it + (lane >> 5), c = lane & 31;
-            const int m = r0 + 64 * pass + r, n = c0 + 4 * c;
+        for (int it = 0; it < ROWS / RPR; ++it) {
+            const int r = RPR * it + lane / CPR, c = lane % CPR;
+            const int m = r0 + ROWS * pass + r, n = c0 + 4 * c;
             if (m < p.M && n < p.N) {
                 f32x4 x = *reinterpret_cast<const f32x4 *>(stage + r * ROWB + ((c ^ (r & 15)) * 16));
                 store_result<OUT>(p, split, m, n, x);
@@ -160,18 +173,23 @@ __device__ __forceinline__ void store_wave_block_any(const KernelArgs &p, const 
     }
 }
 
-template <int IN, int OUT>
+template <int IN, int OUT, int BN>
 __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
 {
-    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int BM = 256, BK = 64;
     constexpr int PITCH = 128;                // bytes per LDS row (64 16-bit values)
     constexpr int CH = 8;                     // 16-byte chunks per row
-    constexpr int UNIT = 256 * PITCH;         // one operand of one slab, 32 KB
-    constexpr int UNITS = 5;                  // A: units 0, 1; B: units 2, 3, 4
-    constexpr int FM = 4, FN = 4;
-    static_assert(UNITS * UNIT <= 160 * 1024, "LDS budget");
+    constexpr int UA = BM * PITCH;            // A of one slab, 32 KB
+    constexpr int UBB = BN * PITCH;           // B of one slab, 32 or 16 KB
+    constexpr int NUB = (160 * 1024 - 2 * UA) / UBB;   // B units: 3 or 6
+    constexpr int FM = 4, FN = BN / 64;       // wave block 128 x (BN / 2)
+    constexpr int LA = BM / 32, LB = BN / 32; // loads per wave and slab
+    constexpr int MF = FN * FM;               // MFMAs per k-step
+    constexpr int NR = FM + FN;               // fragment reads per k-step
+    static_assert(BN == 256 || BN == 128, "tile");
+    static_assert(2 * UA + NUB * UBB <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[UNITS * UNIT];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * UA + NUB * UBB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -191,35 +209,35 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     const __amdgpu_buffer_rsrc_t rsB =
         make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)rows_b * (uint32_t)p.ldb * 2u);
 
-    // Load j (0..7) of wave w for one operand covers tile rows 32 j + 8 w + lane / 8:
+    // Load j of wave w for one operand covers tile rows 32 j + 8 w + lane / 8:
     // lane l fills physical chunk l % 8 of its row, which holds logical chunk
     // (l % 8) ^ key(row).  The row step 32 keeps the row mod 16, hence the key,
     // the same for every load of the wave.
     const int lr = lane >> 3;
     const int lc = (lane & 7) ^ row_key<CH>(8 * wave + lr);
     const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
-    const uint32_t voffA = (uint32_t)lr * lda2 + (uint32_t)lc * 16u;
-    const uint32_t voffB = (uint32_t)lr * ldb2 + (uint32_t)lc * 16u;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-    // Load j of operand `op` (0: A, 1: B) of local slab i into unit u.  Rows
-    // past the tile's valid rows and chunks at or past K read zeros.  So does a
-    // slab at or past nk: the main loop issues the loads of later slabs on
-    // every step, and past the last slab they fill a unit no later slab reads
-    // with zeros (an out-of-range offset touches no memory), which keeps every
-    // wait count of the loop the same.
+    // Load j of operand `op` (0: A into A unit u, 1: B into B unit u) of local
+    // slab i.  No load is out of range in all its lanes: a load that touches
+    // no memory may count as done before the loads issued ahead of it, which
+    // would let a vmcnt wait pass too early.  So rows past the tile's valid
+    // rows re-read its last valid row (their outputs are never stored), and a
+    // slab at or past nk re-reads the split's last slab: the main loop issues
+    // the loads of later slabs on every step, and past the last slab they fill
+    // a unit no later slab reads, which keeps every wait count of the loop the
+    // same.  Only the chunks at or past K of a row read zeros.
     auto issue_one = [&](int op, int i, int u, int j, auto nt) {
-        const int kt = kt0 + i;
-        const bool kin = i < nk && lc * 8 < p.K - kt * BK;
+        const int kt = kt0 + (i < nk ? i : nk - 1);
+        const bool kin = lc * 8 < p.K - kt * BK;
         const uint32_t kb = (uint32_t)kt * (uint32_t)(BK * 2);
-        const int row = 32 * j + 8 * wave;
-        const uint32_t dst = lds0 + (uint32_t)(u * UNIT + row * PITCH);
+        const int row = 32 * j + 8 * wave + lr;
         if (op == 0) {
-            const uint32_t v = (kin && row + lr < rows_a) ? voffA : kOutOfRange;
-            load_lds16(rsA, v, kb + (uint32_t)row * lda2, dst);
+            const uint32_t v = kin ? (uint32_t)min(row, rows_a - 1) * lda2 + (uint32_t)lc * 16u : kOutOfRange;
+            load_lds16(rsA, v, kb, lds0 + (uint32_t)(u * UA + (row - lr) * PITCH));
         } else {
-            const uint32_t v = (kin && row + lr < rows_b) ? voffB : kOutOfRange;
-            load_lds16_policy<decltype(nt)::value>(rsB, v, kb + (uint32_t)row * ldb2, dst);
+            const uint32_t v = kin ? (uint32_t)min(row, rows_b - 1) * ldb2 + (uint32_t)lc * 16u : kOutOfRange;
+            load_lds16_policy<decltype(nt)::value>(rsB, v, kb, lds0 + (uint32_t)(2 * UA + u * UBB + (row - lr) * PITCH));
         }
     };
 
@@ -238,20 +256,21 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0.0f;
 
-    // Fragment read n (0..7) of k-step ks from units (ua, ub) into buffer `buf`,
-    // in the order the MFMAs below consume them: B block 0, A blocks 0..3, B
-    // blocks 1..3.
+    // Fragment read n (0..NR-1) of k-step ks from A unit ua and B unit ub into
+    // buffer `buf`, in the order the MFMAs below consume them: B block 0, A
+    // blocks 0..3, then the other B blocks.
     auto read_one = [&](int ua, int ub, int ks, int buf, int n) {
         const int off = roff0 ^ (32 * ks);
-        if (n >= 1 && n <= 4)
+        if (n >= 1 && n <= FM)
             fa[buf][n - 1] =
-                *reinterpret_cast<const u32x4 *>(smem + ua * UNIT + off + (wm * 128 + (n - 1) * 32) * PITCH);
+                *reinterpret_cast<const u32x4 *>(smem + ua * UA + off + (wm * 128 + (n - 1) * 32) * PITCH);
         else {
-            const int f = n == 0 ? 0 : n - 4;
-            fb[buf][f] = *reinterpret_cast<const u32x4 *>(smem + ub * UNIT + off + (wn * 128 + f * 32) * PITCH);
+            const int f = n == 0 ? 0 : n - FM;
+            fb[buf][f] = *reinterpret_cast<const u32x4 *>(smem + 2 * UA + ub * UBB + off +
+                                                          (wn * (BN / 2) + f * 32) * PITCH);
         }
     };
-    // MFMA t (0..15) of a k-step on buffer `buf`: B block t / 4 against A block t % 4.
+    // MFMA t (0..MF-1) of a k-step on buffer `buf`: B block t / 4 against A block t % 4.
     auto mfma_one = [&](int buf, int t) {
         acc[t >> 2][t & 3] = mfma32x32x16<IN>(fb[buf][t >> 2], fa[buf][t & 3], acc[t >> 2][t & 3]);
     };
@@ -259,69 +278,77 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     // The main loop for one B load policy (a compile-time flag: the policy is
     // an immediate of the load instruction).  Its body has no branch, so the
     // compiler keeps every accumulator in place across it, and its order is
-    // fixed by scheduling barriers: within each k-step the eight fragment
-    // reads of the next k-step go out beside the first eight MFMAs and four
-    // loads beside MFMAs 2, 5, 8 and 11; the slab's barrier comes before the
-    // last two MFMAs of k-step 2, which keep the matrix core busy while the
-    // waves meet.
+    // fixed by scheduling barriers: within each k-step the fragment reads of
+    // the next k-step go out beside the first MFMAs and the k-step's loads
+    // beside the following ones; the slab's barrier comes before the last two
+    // MFMAs of k-step 2, which keep the matrix core busy while the waves meet.
+    //
+    // Loads: A(i) lives in A unit i mod 2, B(i) in B unit i mod NUB.  The
+    // barrier of slab i frees both units of slab i; A(i + 2) goes into its A
+    // unit in k-step 3 of slab i and k-step 0 of slab i + 1, B(i + NUB) into
+    // its B unit in k-steps 1 and 2 of slab i + 1.  At the barrier of slab i a
+    // wave needs its loads of slab i + 1 landed; only the LB loads of
+    // B(i + NUB - 1) come after them.
     auto main_loop = [&](auto nt) {
-        // Prologue: A(0), B(0), B(1) and the first half of A(1); then slab 0
-        // landed (12 loads of this wave may still be in flight).
+        // Prologue: A(0), B(0) .. B(NUB - 2) and the first half of A(1); then
+        // slab 0 landed.
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < LA; ++j)
             issue_one(0, 0, 0, j, nt);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            issue_one(1, 0, 2, j, nt);
+        for (int b = 0; b < NUB - 1; ++b)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            issue_one(1, 1, 3, j, nt);
+            for (int j = 0; j < LB; ++j)
+                issue_one(1, b, b, j, nt);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < LA / 2; ++j)
             issue_one(0, 1, 1, j, nt);
-        wait_vmcnt<12>();
+        wait_vmcnt<(NUB - 2) * LB + LA / 2>();
         wg_barrier();
 #pragma unroll
-        for (int n = 0; n < 8; ++n)
-            read_one(0, 2, 0, 0, n);
+        for (int n = 0; n < NR; ++n)
+            read_one(0, 0, 0, 0, n);
 
-        // One k-step: MFMAs t0..t1-1 on buffer mbuf, with read t (t < 8) of
-        // k-step rks from units (rua, rub) into rbuf and load t / 3 (t = 2, 5,
-        // 8, 11) of `load`.
-        auto kstep = [&](int mbuf, int rua, int rub, int rks, int rbuf, auto load, int t0, int t1) {
+        // One k-step: MFMAs t0..t1-1 on buffer mbuf, with read t (t < NR) of
+        // k-step rks from units (rua, rub) into rbuf and load number k of `load`
+        // beside MFMA 1 + k (MF - 3) / nl (k < nl), so that every load of a
+        // k-step goes out before its last two MFMAs.
+        auto kstep = [&](int mbuf, int rua, int rub, int rks, int rbuf, auto load, int nl, int t0, int t1) {
 #pragma unroll
             for (int t = t0; t < t1; ++t) {
                 mfma_one(mbuf, t);
-                if (t < 8)
+                if (t < NR)
                     read_one(rua, rub, rks, rbuf, t);
-                if (t % 3 == 2 && t <= 11)
-                    load(t / 3);
+#pragma unroll
+                for (int k = 0; k < nl; ++k)
+                    if (t == 1 + k * (MF - 3) / nl)
+                        load(k);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
 
-        int ua = 0, ub = 2;                                 // units of slab i
+        int ua = 0, ub = 0;                                 // units of slab i
         for (int i = 0; i < nk; ++i) {
             const int ua1 = ua ^ 1;                         // A(i + 1), A(i - 1)
-            const int ub1 = ub == 4 ? 2 : ub + 1;           // B(i + 1)
-            const int ub2 = ub == 2 ? 4 : ub - 1;           // B(i + 2) = B(i - 1)
+            const int ub1 = ub == NUB - 1 ? 0 : ub + 1;     // B(i + 1)
+            const int ubp = ub == 0 ? NUB - 1 : ub - 1;     // B(i - 1) = B(i + NUB - 1)
             // k-step 0: the second half of A(i + 1)
-            kstep(0, ua, ub, 1, 1, [&](int j) { issue_one(0, i + 1, ua1, 4 + j, nt); }, 0, 16);
-            // k-steps 1, 2: B(i + 2)
-            kstep(1, ua, ub, 2, 0, [&](int j) { issue_one(1, i + 2, ub2, j, nt); }, 0, 16);
-            auto load_b2 = [&](int j) { issue_one(1, i + 2, ub2, 4 + j, nt); };
-            kstep(0, ua, ub, 3, 1, load_b2, 0, 14);
+            kstep(0, ua, ub, 1, 1, [&](int k) { issue_one(0, i + 1, ua1, LA / 2 + k, nt); }, LA / 2, 0, MF);
+            // k-steps 1, 2: B(i + NUB - 1) into the unit B(i - 1) has left
+            kstep(1, ua, ub, 2, 0, [&](int k) { issue_one(1, i + NUB - 1, ubp, k, nt); }, LB / 2, 0, MF);
+            auto load_b2 = [&](int k) { issue_one(1, i + NUB - 1, ubp, LB / 2 + k, nt); };
+            kstep(0, ua, ub, 3, 1, load_b2, LB / 2, 0, MF - 2);
             // every wave holds this slab's last fragments and has its own loads
-            // of slab i + 1 landed (B(i + 2) may be in flight); the barrier
-            // publishes both
+            // of slab i + 1 landed (B(i + NUB - 1) may be in flight); the
+            // barrier publishes both
             wait_lgkmcnt0();
-            wait_vmcnt<8>();
+            wait_vmcnt<LB>();
             wg_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            kstep(0, ua, ub, 3, 1, load_b2, 14, 16);
+            kstep(0, ua, ub, 3, 1, load_b2, LB / 2, MF - 2, MF);
             // k-step 3: the first fragments of slab i + 1, and the first half of
             // A(i + 2) into the unit A(i) has left
-            kstep(1, ua1, ub1, 0, 0, [&](int j) { issue_one(0, i + 2, ua, j, nt); }, 0, 16);
+            kstep(1, ua1, ub1, 0, 0, [&](int k) { issue_one(0, i + 2, ua, k, nt); }, LA / 2, 0, MF);
             ua = ua1;
             ub = ub1;
         }
@@ -337,23 +364,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     // Epilogue.  Every wave is past its last fragment read and every load has
     // landed; after the barrier the ring is free for staging (32 KB per wave).
     const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
-    const int r0 = m0 + wm * 128, c0 = n0 + wn * 128;
+    const int r0 = m0 + wm * 128, c0 = n0 + wn * (BN / 2);
     uint8_t *stage = smem + wave * 32768;
     wait_vmcnt<0>();
     wg_barrier();
     if (full && p.splits == 1 && p.rows16 && !p.epi) {
         if constexpr (OUT == OUT_BF16)
-            store_wave_block_staged<__bf16, true>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)r0 * p.ldc + c0,
-                                                  p.ldc, lane);
+            store_wave_block_staged<__bf16, FN, true>(
+                acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)r0 * p.ldc + c0, p.ldc, lane);
         else if constexpr (OUT == OUT_FP16)
-            store_wave_block_staged<_Float16, true>(acc, stage,
-                                                    static_cast<_Float16 *>(p.C) + (int64_t)r0 * p.ldc + c0, p.ldc,
-                                                    lane);
+            store_wave_block_staged<_Float16, FN, true>(
+                acc, stage, static_cast<_Float16 *>(p.C) + (int64_t)r0 * p.ldc + c0, p.ldc, lane);
         else
-            store_wave_block_staged<float, true>(acc, stage, static_cast<float *>(p.C) + (int64_t)r0 * p.ldc + c0,
-                                                 p.ldc, lane);
+            store_wave_block_staged<float, FN, true>(
+                acc, stage, static_cast<float *>(p.C) + (int64_t)r0 * p.ldc + c0, p.ldc, lane);
     } else {
-        store_wave_block_any<OUT>(p, acc, stage, r0, c0, split, lane);
+        store_wave_block_any<OUT, FN>(p, acc, stage, r0, c0, split, lane);
     }
 }
 

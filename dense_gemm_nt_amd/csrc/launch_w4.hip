@@ -1,19 +1,24 @@
-// Launch table of the four-wave 256x256 tile (gemm_nt_w4.hpp).
+// Launch tables of the four-wave 256 x BN tiles (gemm_nt_w4.hpp): 256 x 256 and
+// the 256 x 128 decode tile.
 #include "gemm_nt_launch.hpp"
 #include "gemm_nt_w4.hpp"
 
 namespace gnt {
 
-template <int IN, int OUT>
+template <int IN, int OUT, int BN>
 static hipError_t launch_w4(const KernelArgs &a, unsigned grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_nt_w4<IN, OUT>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_nt_w4<IN, OUT, BN>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-LaunchTable kW4 = {
-    {launch_w4<0, 0>, launch_w4<0, 1>, launch_w4<0, 2>},
-    {launch_w4<1, 0>, launch_w4<1, 1>, launch_w4<1, 2>},
-};
+#define GNT_W4_TABLE(BN)                                                                        \
+    {                                                                                           \
+        {launch_w4<0, 0, BN>, launch_w4<0, 1, BN>, launch_w4<0, 2, BN>},                        \
+        {launch_w4<1, 0, BN>, launch_w4<1, 1, BN>, launch_w4<1, 2, BN>},                        \
+    }
+
+LaunchTable kW4 = GNT_W4_TABLE(256);
+LaunchTable kW4_128 = GNT_W4_TABLE(128);
 
 }  // namespace gnt
