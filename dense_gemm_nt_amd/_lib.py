@@ -36,7 +36,7 @@ class GemmPlan(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int),
                 ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("name", ctypes.c_char * 48),
-                ("streamk", ctypes.c_int)]
+                ("streamk", ctypes.c_int), ("inreduce", ctypes.c_int)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}

@@ -23,13 +23,18 @@
 #include "gemm_nt.h"
 #include "gemm_nt_launch.hpp"
 
+// Per-tile arrival counters of the in-kernel two-split reduction, at the end of
+// every workspace (handle or scratch): zero between calls (each call's second
+// arrival resets its tile's counter).
+#define GEMM_COUNTER_BYTES ((int64_t)64 << 10)
+
 // Scratch of gemm_run_noalloc: the split-K / stream-K partials of calls that may
 // not allocate.  Each device the library runs on holds its own copy from the
 // first call on it until the process ends.  In host code the name stands for
 // the host-side shadow, never a device address: the device address comes from
 // hipGetSymbolAddress (per device, see noalloc_scratch) and only that address is
 // passed to kernels.
-static __device__ __align__(256) uint8_t scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+static __device__ __align__(256) uint8_t scratch[GEMM_NOALLOC_SCRATCH_BYTES + GEMM_COUNTER_BYTES];
 
 namespace {
 
@@ -116,6 +121,7 @@ struct Plan {
     int group_m;
     int64_t grid;
     int64_t ws_bytes;
+    int inreduce;          // two K splits reduced inside the kernel (no second pass)
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -131,7 +137,7 @@ int find_config(const char *name)
 // Pick the tile shape and the K split for a problem.  `ws_bytes` bounds the
 // split-K partial storage; `force_cfg` / `force_splits` (>= 0 / > 0) override.
 Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg, int force_splits,
-               int streamk = 0)
+               int streamk = 0, int inreduce = 1)
 {
     Plan p{};
     int cfg;
@@ -241,6 +247,18 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         p.group_m = 1;
     p.grid = tiles * splits;
     p.ws_bytes = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+    // Two K splits on the 256-row tiles: the second split to finish adds the
+    // first's partial (one 256 x BN FP32 slot per split and tile) and stores
+    // the tile, instead of a second pass over [splits][M][N] partials.
+    if (inreduce && splits == 2 &&
+        (cfg == CFG_PP2_256x256 || cfg == CFG_W4_256x256 || cfg == CFG_W4_256x128) &&
+        tiles * 4 <= GEMM_COUNTER_BYTES) {
+        const int64_t need = tiles * 2 * (int64_t)c.bm * c.bn * 4;
+        if (need <= ws_bytes) {
+            p.inreduce = 1;
+            p.ws_bytes = need;
+        }
+    }
 
     // Stream-K (the CuTe page's section 9 names it beside split-K): when the
     // ping-pong tiles with their K splits leave at least 3/8 of the compute
@@ -279,6 +297,7 @@ struct gemm_handle_s {
     int force_cfg;
     int force_splits;
     int persistent;    // GEMM_PERSIST=1: ping-pong tiles run by 256 persistent blocks
+    int inreduce;      // GEMM_INREDUCE: 1 (default) two K splits reduced in the kernel, 0 never
     int streamk;       // GEMM_STREAMK: 0 off, 1 by the plan rule (default), 2 whenever
                        // the ping-pong tile is planned
     int log;
@@ -371,6 +390,7 @@ gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
     out->workgroups = (M == 0 || N == 0) ? 0 : p.grid;
     out->workspace_bytes = p.ws_bytes;
     out->streamk = p.stream;
+    out->inreduce = p.inreduce;
     snprintf(out->name, sizeof(out->name), "%s", c.name);
     return GEMM_OK;
 }
@@ -406,6 +426,9 @@ gemm_status_t gemm_create(gemm_handle_t *out)
     if (const char *e = getenv("GEMM_LOG"))
         h->log = atoi(e);
     h->ws_bytes = mb << 20;
+    h->inreduce = 1;
+    if (const char *e = getenv("GEMM_INREDUCE"))
+        h->inreduce = atoi(e) != 0;
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
         return GEMM_ERR_HIP;
@@ -416,10 +439,19 @@ gemm_status_t gemm_create(gemm_handle_t *out)
             return GEMM_ERR_ALLOC;
         }
     }
-    if (hipMalloc(&h->partials, (size_t)h->ws_bytes) != hipSuccess) {
+    if (hipMalloc(&h->partials, (size_t)(h->ws_bytes + GEMM_COUNTER_BYTES)) != hipSuccess) {
         (void)hipGetLastError();
         delete h;
         return GEMM_ERR_ALLOC;
+    }
+    // the arrival counters start at zero (every call leaves them at zero)
+    if (hipMemset(reinterpret_cast<uint8_t *>(h->partials) + h->ws_bytes, 0, (size_t)GEMM_COUNTER_BYTES) !=
+            hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(h->partials);
+        delete h;
+        return GEMM_ERR_HIP;
     }
     *out = h;
     return GEMM_OK;
@@ -488,11 +520,16 @@ gemm_status_t check_device(gemm_handle_t h)
 // the static scratch of gemm_run_noalloc.
 struct Workspace {
     float *partials;
-    int64_t bytes;
+    int64_t bytes;         // for partials and grouped problem lists
+    unsigned *counters;    // GEMM_COUNTER_BYTES of arrival counters
     int log;
 };
 
-Workspace workspace_of(gemm_handle_t h) { return Workspace{h->partials, h->ws_bytes, h->log}; }
+Workspace workspace_of(gemm_handle_t h)
+{
+    return Workspace{h->partials, h->ws_bytes,
+                     reinterpret_cast<unsigned *>(reinterpret_cast<uint8_t *>(h->partials) + h->ws_bytes), h->log};
+}
 
 // Fill the plan-, output- and epilogue-dependent fields of `a` (whose operand
 // fields the caller has set), then enqueue the kernel and, with split-K, the
@@ -525,6 +562,8 @@ gemm_status_t enqueue(const Workspace &ws, const Plan &p, KernelArgs &a, launch_
     a.partials = ws.partials;
     a.sk_units = p.stream ? (int)p.sk_units : 0;
     a.sk_maxseg = p.sk_maxseg;
+    a.inreduce = p.inreduce;
+    a.counters = ws.counters;
     a.alpha = 1.0f;
     if (epi) {
         a.alpha = epi->alpha;
@@ -539,9 +578,10 @@ gemm_status_t enqueue(const Workspace &ws, const Plan &p, KernelArgs &a, launch_
     if (ws.log)
         fprintf(stderr, "gemm_nt: M=%lld N=%lld K=%lld cfg=%s tiles=%dx%d splits=%d kt/split=%d grid=%lld%s\n",
                 (long long)M, (long long)N, (long long)K, kConfigs[p.cfg].name, p.tiles_m,
-                p.tiles_n, p.splits, p.kt_per_split, (long long)p.grid, p.stream ? " stream-K" : "");
+                p.tiles_n, p.splits, p.kt_per_split, (long long)p.grid,
+                p.stream ? " stream-K" : p.inreduce ? " reduced in-kernel" : "");
     hipError_t e = fn(a, (unsigned)p.grid, stream);
-    if (e == hipSuccess && p.splits > 1)
+    if (e == hipSuccess && p.splits > 1 && !p.inreduce)
         e = launch_splitk_sum(a, out_dtype, stream);
     if (e == hipSuccess && p.stream)
         e = launch_streamk_sum(a, (int)p.grid, out_dtype, stream);
@@ -580,7 +620,7 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     if (!nt && h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
         return GEMM_ERR_UNSUPPORTED;
     const Plan p = make_plan(M, N, K, h->ws_bytes, nt ? h->force_cfg : CFG_PP2_256x256,
-                             h->force_splits, nt ? h->streamk : 0);
+                             h->force_splits, nt ? h->streamk : 0, h->inreduce && !h->persistent);
     KernelArgs a{};
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);
@@ -655,7 +695,8 @@ gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C, int64_t M,
     a.ldb = (int)ldb;
     launch_fn fn = p.stream ? gnt::kPP2_persistent[in_dtype][out_dtype]
                             : kConfigs[p.cfg].fn[in_dtype][out_dtype];
-    const Workspace ws{static_cast<float *>(ptr), GEMM_NOALLOC_SCRATCH_BYTES, 0};
+    const Workspace ws{static_cast<float *>(ptr), GEMM_NOALLOC_SCRATCH_BYTES,
+                       reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ptr) + GEMM_NOALLOC_SCRATCH_BYTES), 0};
     return enqueue(ws, p, a, fn, C, M, N, K, ldc, out_dtype, nullptr, stream);
 }
 
@@ -952,7 +993,7 @@ gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void
     if (h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
         return GEMM_ERR_UNSUPPORTED;
     // A slab is 128 bytes of each row: 128 FP8 values, planned as 64 16-bit ones
-    const Plan p = make_plan(M, N, K / 2, h->ws_bytes, CFG_PP2_256x256, h->force_splits);
+    const Plan p = make_plan(M, N, K / 2, h->ws_bytes, CFG_PP2_256x256, h->force_splits, 0, h->inreduce);
     KernelArgs a{};
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);

@@ -62,9 +62,9 @@ struct KernelArgs {
     int sk_units;          // stream-K: tiles * k_tiles (0: off); block b of the grid G
                            // takes units [b T / G, (b + 1) T / G) in tile-major order
     int sk_maxseg;         // stream-K: partial slots per block
-    int inreduce;          // split-K reduced in the kernel: partials of tile t, split s
-                           // in slot t * splits + s of `partials` (256 KB each, in
-                           // register order), arrivals counted in counters[t]
+    int inreduce;          // two K splits reduced in the kernel: partial of tile t,
+                           // split s in slot 2 t + s of `partials` (in register
+                           // order), arrivals counted in counters[t]
     unsigned *counters;    // per-tile arrival counters, zero between calls
     // fused epilogue D = act(alpha * acc + beta * C_old + bias), applied when epi != 0
     float alpha, beta;
@@ -243,32 +243,31 @@ __device__ __forceinline__ void map_block_split_minor(int bid, int G, int tiles_
     tile_order(t, tiles_m, tiles_n, group_m, tm, tn);
 }
 
-// Split-K reduced inside the GEMM kernel ("A Blackwell GEMM by Hand in CuTe
-// DSL", section 9: split-K for decode, the partials combined by the CTAs
-// themselves instead of a second pass).  Every split of tile t stores its FP32
-// partial, in register order (lane l's register group g of wave w at byte
-// (w * G + g) * 1024 + 16 l of the slot: each store instruction writes 1 KB
-// contiguously), with device-coherent stores, waits for them, and counts its
-// arrival on counters[t].  The split that arrives last adds the other
-// partials to its registers in split order 0, 1, ..., S - 1 (a fixed order:
-// the bits do not depend on which split came last, and equal those of a
-// second pass summing the splits in order), resets the counter for the next
-// call and returns true; the others return false and are done.  No block
-// waits for another, so there is no spin and no dependence on which blocks
-// are resident.  `flag` is a word of LDS no wave is using; every wave of the
-// block calls this with its own accumulators (NW waves, G register groups of
-// four per lane).
+// Two K splits reduced inside the GEMM kernel ("A Blackwell GEMM by Hand in
+// CuTe DSL", section 9: split-K for decode, here with the partials combined by
+// the two CTAs themselves instead of a second pass).  Each split of tile t
+// stores its FP32 partial in register order (lane l's register group g of wave
+// w at byte (w * G + g) * 1024 + 16 l of its slot: each store instruction
+// writes 1 KB contiguously) with device-coherent stores, waits for them, and
+// counts its arrival on counters[t].  The split that arrives second adds the
+// other's partial to its registers as 0 + (own + other): IEEE addition is
+// commutative, so the bits are the same whichever split came second, and they
+// equal those of the ordered second pass, (0 + p0) + p1.  It resets the
+// counter for the next call and returns true; the first returns false and is
+// done.  No block waits for another, so there is no spin and no dependence on
+// which blocks are resident.  `flag` is a word of LDS no wave is using; every
+// wave of the block calls this with its own accumulators (NW waves, G register
+// groups of four per lane).
 template <int NW, int FN, int FM>
-__device__ __forceinline__ bool splitk_arrive(const KernelArgs &p, f32x16 (&acc)[FN][FM], int tile, int split,
-                                              int wave, int lane, uint32_t *flag)
+__device__ __forceinline__ bool splitk2_arrive(const KernelArgs &p, f32x16 (&acc)[FN][FM], int tile, int split,
+                                               int wave, int lane, uint32_t *flag)
 {
     constexpr int G = FN * FM * 4;                        // register groups per lane
     constexpr uint32_t SLOT = (uint32_t)NW * G * 1024u;   // bytes per split partial
-    const int S = p.splits;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(reinterpret_cast<const uint8_t *>(p.partials) + (int64_t)tile * S * SLOT, (uint32_t)S * SLOT);
-    const uint32_t vo = (uint32_t)(wave * G) * 1024u + (uint32_t)lane * 16u;
     constexpr int SC1 = 16;                               // device-coherent access
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const uint8_t *>(p.partials) + (int64_t)tile * 2 * SLOT, 2u * SLOT);
+    const uint32_t vo = (uint32_t)(wave * G) * 1024u + (uint32_t)lane * 16u;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -287,9 +286,10 @@ __device__ __forceinline__ bool splitk_arrive(const KernelArgs &p, f32x16 (&acc)
         *flag = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wg_barrier();
     const uint32_t arrived = __builtin_amdgcn_readfirstlane(*flag);
-    wg_barrier();                                         // everyone has read the flag
-    if ((int)arrived != S - 1)
+    wg_barrier();                                         // every wave has read the flag
+    if (arrived == 0)
         return false;
+    const uint32_t other = (uint32_t)(split ^ 1) * SLOT;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -297,16 +297,11 @@ __device__ __forceinline__ bool splitk_arrive(const KernelArgs &p, f32x16 (&acc)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int g = (fn * FM + fm) * 4 + q;
-                const f32x4 own = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
-                                   acc[fn][fm][4 * q + 3]};
-                f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-                for (int s = 0; s < S; ++s)
-                    sum += s == split ? own
-                                      : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                      rs, vo + g * 1024u, (uint32_t)s * SLOT, SC1));
+                const f32x4 o = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo + g * 1024u, other, SC1));
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[fn][fm][4 * q + e] = sum[e];
+                    acc[fn][fm][4 * q + e] = 0.0f + (acc[fn][fm][4 * q + e] + o[e]);
             }
     if (wave == 0 && lane == 0)
         __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

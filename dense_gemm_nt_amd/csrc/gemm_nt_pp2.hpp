@@ -492,6 +492,14 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     for (int e = 0; e < 16; ++e)
                         acc[fn][fm][e] *= s[fm];
         }
+        if (p.inreduce) {
+            // two K splits: the second to arrive holds the sum and stores it as
+            // an unsplit tile (the flag lives in unit 8, past the staging area)
+            if (!splitk2_arrive<8, FN, FM>(p, acc, tm * p.tiles_n + tn, split, wave, lane,
+                                           reinterpret_cast<uint32_t *>(smem + 8 * UNIT)))
+                return;
+            p.splits = 1;
+        }
         const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
         uint8_t *stage = smem + wave * 16384;
         if (streamk) {
@@ -615,7 +623,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             wg_barrier();
         }
     } else {
-        map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+        if (p.inreduce)
+            map_block_split_minor(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, tm, tn,
+                                  split);
+        else
+            map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
         tile(tm, tn, split);
     }
 }

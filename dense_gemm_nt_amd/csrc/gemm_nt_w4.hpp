@@ -197,7 +197,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     const int wm = wave >> 1, wn = wave & 1;
 
     int tm, tn, split;
-    map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+    if (p.inreduce)
+        map_block_split_minor(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, tm, tn, split);
+    else
+        map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt0 = split * p.kt_per_split;
     const int nk = min(p.k_tiles, kt0 + p.kt_per_split) - kt0;
@@ -361,6 +364,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
             main_loop(std::false_type{});
     }
 
+    if (p.inreduce) {
+        // two K splits: the second to arrive holds the sum and stores it as an
+        // unsplit tile
+        wait_vmcnt<0>();
+        if (!splitk2_arrive<4, FN, FM>(p, acc, tm * p.tiles_n + tn, split, wave, lane,
+                                       reinterpret_cast<uint32_t *>(smem)))
+            return;
+        p.splits = 1;
+    }
     // Epilogue.  Every wave is past its last fragment read and every load has
     // landed; after the barrier the ring is free for staging (32 KB per wave).
     const bool full = m0 + BM <= p.M && n0 + BN <= p.N;

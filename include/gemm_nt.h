@@ -67,7 +67,10 @@ typedef enum {
 } gemm_status_t;
 
 /* Create a handle on the current device: allocates the workspace for split-K
- * and stream-K partials (128 MiB by default; GEMM_WORKSPACE_MB overrides).
+ * and stream-K partials (128 MiB by default; GEMM_WORKSPACE_MB overrides) and
+ * 64 KiB of per-tile counters, which it zeroes (synchronously) and which every
+ * call leaves at zero.  GEMM_INREDUCE=0 turns the in-kernel reduction of two
+ * K splits off (every split plan then takes the second pass).
  * *out is NULL on error.  For measurement, GEMM_CONFIG=<name> forces one kernel
  * configuration, GEMM_SPLITS=<n> a K split on every call of this handle, and
  * GEMM_STREAMK=0/1/2 turns stream-K off, leaves it to the plan (default) or
@@ -103,9 +106,10 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C,
  *   Every call on one device shares that device's scratch: two calls that may
  *   run concurrently on one device (different streams, or different host
  *   threads without ordering) race on it.  Serialise them, e.g. on one stream.
- *   Nothing in the scratch has to start at zero; each call writes every
- *   partial it reads. */
-#define GEMM_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+ *   Each call writes every partial it reads; the array's per-tile counters
+ *   start at zero when the library is loaded and every call leaves them at
+ *   zero. */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)   /* partials; plus 64 KiB of counters */
 gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C,
                                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                                int64_t ldc, int in_dtype, int out_dtype, hipStream_t stream);
@@ -278,11 +282,14 @@ typedef struct {
     int lds_bytes;                 /* LDS the kernel allocates per workgroup */
     int64_t tiles;                 /* output tiles */
     int64_t workgroups;            /* grid size */
-    int64_t workspace_bytes;       /* split-K partials used (splits * M * N * 4), or the
+    int64_t workspace_bytes;       /* split-K partials used (splits * M * N * 4; with
+                                      inreduce, tiles * 2 * block_m * block_n * 4), or the
                                       stream-K slots (workgroups * segments * 256 KB) */
     char name[48];                 /* kernel configuration name */
     int streamk;                   /* 1: stream-K (each workgroup an equal run of the
                                       tiles * k-slabs units, then a reduction kernel) */
+    int inreduce;                  /* 1: two K splits whose second to finish adds the
+                                      first's partial and stores the tile (no second pass) */
 } gemm_plan_t;
 
 gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,

@@ -20,13 +20,19 @@ def say(msg):
     sys.stdout.flush()
 
 
-def new_handle(config=None, splits=None, persistent=False, streamk=None):
+def new_handle(config=None, splits=None, persistent=False, streamk=None, inreduce=None):
     """A fresh library handle; `config` / `splits` force the plan for this handle,
     `persistent` runs its ping-pong tiles with persistent blocks, `streamk`
-    (0 / 1 / 2) sets its stream-K mode (default: the plan rule)."""
+    (0 / 1 / 2) sets its stream-K mode (default: the plan rule), `inreduce`
+    (0 / 1) the in-kernel reduction of two K splits (default: on)."""
     from dense_gemm_nt_amd import Gemm
-    old = {k: os.environ.get(k) for k in ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_PERSIST", "GEMM_STREAMK")}
+    old = {k: os.environ.get(k) for k in ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_PERSIST", "GEMM_STREAMK",
+                                          "GEMM_INREDUCE")}
     try:
+        if inreduce is not None:
+            os.environ["GEMM_INREDUCE"] = str(inreduce)
+        else:
+            os.environ.pop("GEMM_INREDUCE", None)
         if streamk is not None:
             os.environ["GEMM_STREAMK"] = str(streamk)
         else:

@@ -162,6 +162,15 @@ def test_plan_regimes(g):
     assert p["name"] == "32x128x64_w4_s6" and p["splits"] == 3
     assert g.gemm_plan(64, 8192, 8192)["name"] == "32x128x64_w4_s6"
     assert g.gemm_plan(96, 28672, 8192)["name"] == "128x128x64_w4_s4"
+    # two K splits on the 256-row tiles are reduced inside the kernel (one
+    # 256 x 256 FP32 slot per split and tile); more splits take the second pass
+    p = g.gemm_plan(256, 28672, 8192)
+    assert p["splits"] == 2 and p["inreduce"] == 1
+    assert p["workspace_bytes"] == p["tiles"] * 2 * p["block_m"] * p["block_n"] * 4
+    p = g.gemm_plan(256, 8192, 8192)
+    assert p["splits"] > 2 and p["inreduce"] == 0
+    assert p["workspace_bytes"] == p["splits"] * 256 * 8192 * 4
+    assert g.gemm_plan(4096, 4096, 4096)["inreduce"] == 0
     # the 4 KB stride rule only moves a split count the fill rule chose: with
     # at least 256 tiles there is one split, and it stays one
     p = g.gemm_plan(1, 65536, 8192)
