@@ -95,7 +95,6 @@ const Config kConfigs[] = {
     {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk},
     {"128x128x64_w4_s2", 128, 128, 64, 4, 2, 65536, 0, 1, gnt::kTile128x128_w4_s2},
     {"32x128x64_w4_s6", 32, 128, 64, 4, 6, 122880, 0, 1, gnt::kTile32x128_w4_s6},
-    {"256x256x64_w4_u5", 256, 256, 64, 4, 5, 163840, 0, 1, gnt::kW4},
     {"256x128x64_w4_u8", 256, 128, 64, 4, 8, 163840, 0, 1, gnt::kW4_128},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
@@ -105,8 +104,7 @@ enum {
     CFG_PP2_256x256 = 2,
     CFG_W4_128x128_S2 = 3,
     CFG_W4_32x128 = 4,
-    CFG_W4_256x256 = 5,
-    CFG_W4_256x128 = 6,
+    CFG_W4_256x128 = 5,
 };
 
 struct Plan {
@@ -156,7 +154,17 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         // Decode batches: the whole of M in one 256-row tile of the ping-pong
         // kernel (A stays in L2, every compute unit streams its own 256-row
         // panel of B), and split-K below to bring the grid up to the machine.
+        // When that tile would need more than four K splits with K up to 16384
+        // (few N tiles: 256 x 10240 x 8192, 256 x 8192 x 8192), the four-wave
+        // 256 x 128 tile fills the machine with half as many splits, i.e. half
+        // the FP32 partial traffic (measured 67.6 -> 59.5 us at 256 x 10240 x 8192,
+        // even at 256 x 8192 x 8192; slower at 256 x 8192 x 28672, whose long K
+        // the ping-pong tile splits eight ways, and at 256 x 28672 x 8192).
         cfg = CFG_PP2_256x256;
+        const int64_t t256 = cdiv(N, 256), kt64 = cdiv(K, 64);
+        const int64_t s256 = std::min<int64_t>(kNumCUs / std::max<int64_t>(1, t256), kt64 / 20);
+        if (t256 < kNumCUs && s256 > 4 && K <= 16384)
+            cfg = CFG_W4_256x128;
     } else {
         // The 256x256 ping-pong tile when its blocks fill at least half the
         // machine, with the K splits the split rule below would give it (at
@@ -251,7 +259,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     // first's partial (one 256 x BN FP32 slot per split and tile) and stores
     // the tile, instead of a second pass over [splits][M][N] partials.
     if (inreduce && splits == 2 &&
-        (cfg == CFG_PP2_256x256 || cfg == CFG_W4_256x256 || cfg == CFG_W4_256x128) &&
+        (cfg == CFG_PP2_256x256 || cfg == CFG_W4_256x128) &&
         tiles * 4 <= GEMM_COUNTER_BYTES) {
         const int64_t need = tiles * 2 * (int64_t)c.bm * c.bn * 4;
         if (need <= ws_bytes) {
@@ -630,7 +638,7 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
                       : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
     Plan q = p;
     if (p.stream) {
-        fn = gnt::kPP2_persistent[in_dtype][out_dtype];   // its stream-K mode
+        fn = gnt::kPP2_streamk[in_dtype][out_dtype];
     } else if (nt && h->persistent && p.cfg == CFG_PP2_256x256 && p.grid > kNumCUs) {
         fn = gnt::kPP2_persistent[in_dtype][out_dtype];
         q.grid = kNumCUs;
@@ -693,7 +701,7 @@ gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C, int64_t M,
     a.B = static_cast<const uint16_t *>(B);
     a.lda = (int)lda;
     a.ldb = (int)ldb;
-    launch_fn fn = p.stream ? gnt::kPP2_persistent[in_dtype][out_dtype]
+    launch_fn fn = p.stream ? gnt::kPP2_streamk[in_dtype][out_dtype]
                             : kConfigs[p.cfg].fn[in_dtype][out_dtype];
     const Workspace ws{static_cast<float *>(ptr), GEMM_NOALLOC_SCRATCH_BYTES,
                        reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ptr) + GEMM_NOALLOC_SCRATCH_BYTES), 0};

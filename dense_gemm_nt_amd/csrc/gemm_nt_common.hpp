@@ -279,6 +279,9 @@ __device__ __forceinline__ bool splitk2_arrive(const KernelArgs &p, f32x16 (&acc
                                  acc[fn][fm][4 * q + 3]};
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, vo + g * 1024u,
                                                        (uint32_t)split * SLOT, SC1);
+                // a few stores at a time, so the accumulators are not all copied out first
+                if ((g & 3) == 3)
+                    __builtin_amdgcn_sched_barrier(0);
             }
     wait_vmcnt<0>();
     wg_barrier();
@@ -302,6 +305,10 @@ __device__ __forceinline__ bool splitk2_arrive(const KernelArgs &p, f32x16 (&acc
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[fn][fm][4 * q + e] = 0.0f + (acc[fn][fm][4 * q + e] + o[e]);
+                // eight loads in flight at a time: enough to cover the latency,
+                // few enough registers to keep every accumulator in place
+                if ((g & 7) == 7)
+                    __builtin_amdgcn_sched_barrier(0);
             }
     if (wave == 0 && lane == 0)
         __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

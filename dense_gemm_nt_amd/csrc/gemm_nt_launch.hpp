@@ -28,9 +28,10 @@ extern LaunchTable kPP2_f8_e4e4_grouped, kPP2_f8_e4e5_grouped, kPP2_f8_e5e4_grou
     kPP2_f8_e5e5_grouped;
 // grouped launches (16-bit inputs, K-major operands), [in dtype][out dtype]
 extern LaunchTable kPP2_grouped;
-// persistent blocks over the tiles of one problem (16-bit, K-major)
-extern LaunchTable kPP2_persistent;
-// the four-wave 256x256 and 256x128 tiles (gemm_nt_w4.hpp), 16-bit, K-major
-extern LaunchTable kW4, kW4_128;
+// persistent blocks over the tiles of one problem, and its stream-K form
+// (16-bit, K-major)
+extern LaunchTable kPP2_persistent, kPP2_streamk;
+// the four-wave 256x128 tile (gemm_nt_w4.hpp), 16-bit, K-major
+extern LaunchTable kW4_128;
 
 }  // namespace gnt

@@ -66,8 +66,10 @@
 
 namespace gnt {
 
+// PS: 0 one tile (split) per block; 1 persistent blocks looping over tiles;
+// 2 stream-K segments, each stored as an FP32 partial slot (no epilogue).
 template <int IN, int OUT, bool AM = false, bool BNM = false, int SC = 0, bool GR = false,
-          bool PS = false>
+          int PS = 0>
 __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
 {
     constexpr bool F8 = IN >= IN_F8;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
 
     KernelArgs p = p0;
 
-    const bool streamk = PS && p.sk_units > 0;
+    constexpr bool streamk = PS == 2;
 
     // One output tile (split `split` of tile (tm, tn)): prologue, main loop and
     // epilogue.  Run once per block, or in a loop by persistent blocks.  A
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // offsets derived from it are recomputed per work unit instead of
         // being held across the epilogue.
         int lane = lane_id;
-        if constexpr (PS)
+        if constexpr (PS != 0)
             asm volatile("" : "+v"(lane));
         const int split = split_;
         const int m0 = tm * BM, n0 = tn * BN;
@@ -138,6 +140,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         const int lrow0 = q * 8 + lane / CH;
         const int lc = (lane % CH) ^ row_key<CH>(lrow0);
         const uint32_t lda2 = (uint32_t)p.lda * ESZ, ldb2 = (uint32_t)p.ldb * ESZ;   // row pitch, bytes
+        const uint32_t voffA = (uint32_t)lrow0 * lda2 + (uint32_t)lc * 16u;
+        const uint32_t voffB = (uint32_t)lrow0 * ldb2 + (uint32_t)lc * 16u;
         const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
         // Load number j (0..3) of the 128-row unit starting at tile row `row0` of
@@ -176,17 +180,15 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                 const uint32_t v = (uint32_t)(4 * q + (lane >> 4)) * ld2 + (uint32_t)col * 2u;
                 load_lds16_policy<NT>(rs, v, (uint32_t)(16 * j) * ld2, dst);
             } else {
-                // rows past the tile's valid rows re-read its last valid row
-                // (their outputs are never stored): a load out of range in every
-                // lane touches no memory and may count as done before the loads
-                // issued ahead of it, and the vmcnt waits count on issue order
+                // rows past the tile's valid rows read zeros (see a_exact below
+                // for the waits that count on them)
                 const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * ESZ);
                 const bool kin = lc * 16 < (p.K - kt * BK) * ESZ;
+                const int row = row0 + 32 * j;
                 const int rows = IS_A ? rows_a : rows_b;
                 const uint32_t ld2 = IS_A ? lda2 : ldb2;
-                const uint32_t r = (uint32_t)min(lrow0 + row0 + 32 * j, rows - 1);
-                const uint32_t v = kin ? r * ld2 + (uint32_t)lc * 16u : kOutOfRange;
-                load_lds16_policy<NT>(IS_A ? rsA : rsB, v, koff, dst);
+                const uint32_t v = (kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange;
+                load_lds16_policy<NT>(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2, dst);
             }
         };
         // The eight loads a wave issues in one memory phase, n = 0..7: group 0
@@ -402,7 +404,16 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // waves skip their fragment reads and MFMAs: they still load A for group
         // 0 and keep every barrier, and their accumulators, never stored, stay 0.
         // (Not in the persistent kernel, whose registers it would overflow.)
-        const bool g1_rows = PS || m0 + 128 < p.M;
+        const bool g1_rows = PS != 0 || m0 + 128 < p.M;
+        // Group 1 waits with the loads of a later A slab in flight.  A load out
+        // of range in every lane touches no memory and may count as done ahead
+        // of the loads issued before it, which would let such a wait pass
+        // early; K-major A rows past M are such loads, and so are the k-rows
+        // past K of an MN-major A's last slab.  So the count-based waits are
+        // used only when no A load of the tile is wholly out of range: a
+        // K-major A with all 256 rows inside M (MN-major columns past M are
+        // clamped instead), and never with the MN-major last slab in flight.
+        const bool a_exact = AM || rows_a == BM;
         if (nk > 0) {
             // Prologue: B(0) by group 0; A(0), A(1) by group 1.  Slab 0 lands before
             // phase 0; A(1) by the end of phase 1 (the steady-state wait).
@@ -416,10 +427,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                 issue_loads(G1{}, 0, std::false_type{});
                 if (nk > 1)
                     issue_loads(G1{}, 1, std::false_type{});
-                // An MN-major A slab's k-rows past K are loads out of range in
-                // every lane (they must read zeros) and may count as done early:
-                // no wait counts past the last slab there.
-                if (nk > 2 || (nk == 2 && !AM))
+                if (a_exact && (nk > 2 || (nk == 2 && !AM)))
                     wait_vmcnt<A_INFLIGHT>();
                 else
                     wait_vmcnt<0>();
@@ -461,7 +469,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     memory_phase(G1{}, i, i + 2 < nk, i + 2, std::false_type{}, g1_rows);   // A(i+2)
                     wait_lgkmcnt0();
                     GNT_PP2_EVENT(i, 3);
-                    if (i + 3 < nk || (i + 2 < nk && !AM))     // A(i+1) landed
+                    if (a_exact && (i + 3 < nk || (i + 2 < nk && !AM)))   // A(i+1) landed
                         wait_vmcnt<A_INFLIGHT>();
                     else
                         wait_vmcnt<0>();
@@ -492,55 +500,58 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     for (int e = 0; e < 16; ++e)
                         acc[fn][fm][e] *= s[fm];
         }
-        if (p.inreduce) {
-            // two K splits: the second to arrive holds the sum and stores it as
-            // an unsplit tile (the flag lives in unit 8, past the staging area)
-            if (!splitk2_arrive<8, FN, FM>(p, acc, tm * p.tiles_n + tn, split, wave, lane,
-                                           reinterpret_cast<uint32_t *>(smem + 8 * UNIT)))
-                return;
-            p.splits = 1;
+        if constexpr (PS == 0 && !GR) {
+            if (p.inreduce) {
+                // two K splits: the second to arrive holds the sum and stores it
+                // as an unsplit tile (the flag lives in unit 8, past the staging
+                // area)
+                if (!splitk2_arrive<8, FN, FM>(p, acc, tm * p.tiles_n + tn, split, wave, lane,
+                                               reinterpret_cast<uint32_t *>(smem + 8 * UNIT)))
+                    return;
+                p.splits = 1;
+            }
         }
-        const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
         uint8_t *stage = smem + wave * 16384;
-        if (streamk) {
+        if constexpr (streamk) {
             // a whole 256 x 256 slot per segment, ragged tiles included
             float *ws = p.partials + (int64_t)sk_slot * (BM * BN);
             store_block_staged<float>(acc, stage, ws + wm0 * BN + wn0, BN, lane);
-            return;
-        }
-        if (full && p.splits > 1 && (p.N & 3) == 0) {
-            float *ws = p.partials + (int64_t)split * p.M * p.N;
-            store_block_staged<float>(acc, stage, ws + (int64_t)(m0 + wm0) * p.N + (n0 + wn0), p.N, lane);
-            return;
-        }
-        if (full && p.splits == 1 && p.rows16 && p.epi) {
-            store_block_staged_epi<OUT>(p, acc, stage, m0 + wm0, n0 + wn0, lane);
-            return;
-        }
-        if (full && p.splits == 1 && p.rows16) {
-            if constexpr (OUT == OUT_BF16)
-                store_block_staged<__bf16, true>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
-            else if constexpr (OUT == OUT_FP16)
-                store_block_staged<_Float16, true>(acc, stage, static_cast<_Float16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
-            else
-                store_block_staged<float, true>(acc, stage, static_cast<float *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
-            return;
-        }
-    #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int m = m0 + wm0 + fm * 32 + (lane & 31);
-            if (m >= p.M)
-                continue;
-    #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-    #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn0 + fn * 32 + 8 * g + 4 * (lane >> 5);
-                    if (n >= p.N)
-                        continue;
-                    f32x4 x = {acc[fn][fm][4 * g], acc[fn][fm][4 * g + 1], acc[fn][fm][4 * g + 2],
-                               acc[fn][fm][4 * g + 3]};
-                    store_result<OUT>(p, split, m, n, x);
+        } else {
+            const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+            if (full && p.splits > 1 && (p.N & 3) == 0) {
+                float *ws = p.partials + (int64_t)split * p.M * p.N;
+                store_block_staged<float>(acc, stage, ws + (int64_t)(m0 + wm0) * p.N + (n0 + wn0), p.N, lane);
+                return;
+            }
+            if (full && p.splits == 1 && p.rows16 && p.epi) {
+                store_block_staged_epi<OUT>(p, acc, stage, m0 + wm0, n0 + wn0, lane);
+                return;
+            }
+            if (full && p.splits == 1 && p.rows16) {
+                if constexpr (OUT == OUT_BF16)
+                    store_block_staged<__bf16, true>(acc, stage, static_cast<__bf16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+                else if constexpr (OUT == OUT_FP16)
+                    store_block_staged<_Float16, true>(acc, stage, static_cast<_Float16 *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+                else
+                    store_block_staged<float, true>(acc, stage, static_cast<float *>(p.C) + (int64_t)(m0 + wm0) * p.ldc + (n0 + wn0), p.ldc, lane);
+                return;
+            }
+        #pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = m0 + wm0 + fm * 32 + (lane & 31);
+                if (m >= p.M)
+                    continue;
+        #pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+        #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int n = n0 + wn0 + fn * 32 + 8 * g + 4 * (lane >> 5);
+                        if (n >= p.N)
+                            continue;
+                        f32x4 x = {acc[fn][fm][4 * g], acc[fn][fm][4 * g + 1], acc[fn][fm][4 * g + 2],
+                                   acc[fn][fm][4 * g + 3]};
+                        store_result<OUT>(p, split, m, n, x);
+                    }
                 }
             }
         }
@@ -584,27 +595,25 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         split = 0;
         tile_order(v - u32(d->tile_start), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
         tile(tm, tn, split);
-    } else if constexpr (PS) {
-        if (streamk) {
-            // Stream-K: block b takes the contiguous units [b T / G, (b + 1) T / G)
-            // of the T = tiles * k_tiles (tile, k-slab) units in tile-major order,
-            // one segment per tile it touches; a barrier between segments, as
-            // between the persistent loop's units below.
-            // (T < 2^31, checked by the host; the values are wave-uniform)
-            auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
-            const int T = uni(p.sk_units), G = uni((int)gridDim.x);
-            int u = uni((int)((int64_t)blockIdx.x * T / G));
-            const int end = uni((int)((int64_t)(blockIdx.x + 1) * T / G));
-            for (int seg = 0; u < end; ++seg) {
-                const int t = uni(u / p.k_tiles);
-                const int e = min(end, (t + 1) * p.k_tiles);
-                tile(uni(t / p.tiles_n), uni(t % p.tiles_n), 0, uni(u - t * p.k_tiles), uni(e - u),
-                     uni((int)blockIdx.x * p.sk_maxseg + seg));
-                wg_barrier();
-                u = e;
-            }
-            return;
+    } else if constexpr (PS == 2) {
+        // Stream-K: block b takes the contiguous units [b T / G, (b + 1) T / G)
+        // of the T = tiles * k_tiles (tile, k-slab) units in tile-major order,
+        // one segment per tile it touches; a barrier between segments, as
+        // between the persistent loop's units below.
+        // (T < 2^31, checked by the host; the values are wave-uniform)
+        auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+        const int T = uni(p.sk_units), G = uni((int)gridDim.x);
+        int u = uni((int)((int64_t)blockIdx.x * T / G));
+        const int end = uni((int)((int64_t)(blockIdx.x + 1) * T / G));
+        for (int seg = 0; u < end; ++seg) {
+            const int t = uni(u / p.k_tiles);
+            const int e = min(end, (t + 1) * p.k_tiles);
+            tile(uni(t / p.tiles_n), uni(t % p.tiles_n), 0, uni(u - t * p.k_tiles), uni(e - u),
+                 uni((int)blockIdx.x * p.sk_maxseg + seg));
+            wg_barrier();
+            u = e;
         }
+    } else if constexpr (PS == 1) {
         // Persistent blocks (grid a multiple of 8, at most the work units):
         // XCD x (the blocks with id % 8 == x) owns the contiguous run
         // [x T / 8, (x + 1) T / 8) of the T work units in tile order, and its

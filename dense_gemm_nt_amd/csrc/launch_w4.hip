@@ -1,5 +1,4 @@
-// Launch tables of the four-wave 256 x BN tiles (gemm_nt_w4.hpp): 256 x 256 and
-// the 256 x 128 decode tile.
+// Launch table of the four-wave 256 x 128 decode tile (gemm_nt_w4.hpp).
 #include "gemm_nt_launch.hpp"
 #include "gemm_nt_w4.hpp"
 
@@ -18,7 +17,6 @@ static hipError_t launch_w4(const KernelArgs &a, unsigned grid, hipStream_t s)
         {launch_w4<1, 0, BN>, launch_w4<1, 1, BN>, launch_w4<1, 2, BN>},                        \
     }
 
-LaunchTable kW4 = GNT_W4_TABLE(256);
 LaunchTable kW4_128 = GNT_W4_TABLE(128);
 
 }  // namespace gnt

@@ -167,9 +167,15 @@ def test_plan_regimes(g):
     p = g.gemm_plan(256, 28672, 8192)
     assert p["splits"] == 2 and p["inreduce"] == 1
     assert p["workspace_bytes"] == p["tiles"] * 2 * p["block_m"] * p["block_n"] * 4
-    p = g.gemm_plan(256, 8192, 8192)
-    assert p["splits"] > 2 and p["inreduce"] == 0
+    p = g.gemm_plan(256, 8192, 28672)
+    assert p["name"] == "256x256x64_w8_pp2" and p["splits"] > 2 and p["inreduce"] == 0
     assert p["workspace_bytes"] == p["splits"] * 256 * 8192 * 4
+    # decode shapes the ping-pong tile would split more than four ways with a
+    # moderate K: the 256x128 tile with half the splits
+    for N in (10240, 8192):
+        p = g.gemm_plan(256, N, 8192)
+        assert p["name"] == "256x128x64_w4_u8" and p["splits"] in (3, 4), p
+    assert g.gemm_plan(256, 28672, 8192)["name"] == "256x256x64_w8_pp2"
     assert g.gemm_plan(4096, 4096, 4096)["inreduce"] == 0
     # the 4 KB stride rule only moves a split count the fill rule chose: with
     # at least 256 tiles there is one split, and it stays one

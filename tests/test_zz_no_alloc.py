@@ -32,7 +32,8 @@ def _noalloc(A_store, B_store, K, in_dt, out_dt):
 
 def test_two_calls_in_a_row_match_gemm_run():
     h = new_handle()
-    # first call: a split-K plan (six splits, 50 MB of partials in the scratch)
+    # first call: a split-K plan (the 256x128 tile, four splits, 32 MB of
+    # partials in the scratch)
     M, N, K = 256, 8192, 8192
     say("case noalloc 1: M=%d N=%d K=%d bf16->bf16" % (M, N, K))
     A, B = make_operands(M, N, K, "bf16", "llm", seed=3)
