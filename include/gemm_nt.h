@@ -75,7 +75,11 @@ typedef enum {
  * configuration, GEMM_SPLITS=<n> a K split on every call of this handle, and
  * GEMM_STREAMK=0/1/2 turns stream-K off, leaves it to the plan (default) or
  * uses it whenever the 256 x 256 ping-pong tile is planned; a GEMM_CONFIG that
- * names no configuration makes gemm_create return GEMM_ERR_INVALID_ARG. */
+ * names no configuration makes gemm_create return GEMM_ERR_INVALID_ARG.
+ * GEMM_PERSIST=1 runs planned 256 x 256 ping-pong grids of more than 256
+ * blocks with 256 persistent blocks.  GEMM_LOG=1 prints each call's plan to
+ * stderr.  GEMM_TEST_FAIL_ALLOC=1 makes gemm_create fail as a failed workspace
+ * allocation does (GEMM_ERR_ALLOC, *out NULL), to test callers' error paths. */
 gemm_status_t gemm_create(gemm_handle_t *out);
 
 /* C = A . B^T (see the top of this file).
