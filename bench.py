@@ -356,6 +356,7 @@ def time_config(g, cfg, iters=50, warmup=10, check=True):
                     "workgroups": plan["workgroups"]}}
     if r.bound == "hbm":
         rec["gbs"] = round(r.bytes / (med * 1e-6) / 1e9, 1)
+    rec["traffic"] = traffic_for("%dx%dx%d %s->%s" % (M, N, K, in_dt, out_dt), plan)
     if check:
         t0 = time.perf_counter()
         rec["parity_worst_err_over_bound"] = round(
@@ -501,7 +502,7 @@ def main():
                    "parity_worst_err_over_bound": worst},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("4096^3 bf16->bf16", plan),
+                     "traffic": traffic_for("4096x4096x4096 bf16->bf16", plan),
                      "kernel_avg_us": round(event_ms * 1e3, 3)},
     }
 

@@ -19,6 +19,7 @@ if ROOT not in sys.path:
 
 WORKLOADS = {
     # name: (M, N, K, in, out, dist, rotating sets)
+    "square512": (512, 512, 512, "bf16", "fp32", "uniform", 8),
     "square4096": (4096, 4096, 4096, "bf16", "bf16", "uniform", 6),
     "square4096_fp16": (4096, 4096, 4096, "fp16", "bf16", "uniform", 6),
     "prefill8192": (8192, 8192, 8192, "bf16", "bf16", "llm", 2),

@@ -99,16 +99,18 @@ def counters(path, skip):
 
 
 def kernel_hash():
-    """Same hash bench.py compares against: the device sources of the NT
-    ping-pong kernel as they are now (host-side planning is checked separately,
-    by the plan recorded beside the counters)."""
+    """Same hash bench.py compares against: every source file of the library
+    (all kernels, their launch tables and the host planner) as it is now; the
+    plan is recorded beside the counters too."""
     import hashlib
     import os
-    root = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
     h = hashlib.sha256()
-    for f in ("gemm_nt_common.hpp", "gemm_nt_pp2.hpp", "gemm_nt_launch.hpp", "launch_pp2.hip"):
-        with open(os.path.join(root, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(root)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode() + b"\0")
+            with open(os.path.join(root, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
