@@ -84,6 +84,10 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libgemm_nt.so is not built; run `python -m dense_gemm_nt_amd.build` "
                            "or __graft_entry__.build() first")
+    # torch first: it carries its own copy of the HIP runtime, and the library
+    # must bind to the one torch's memory and streams come from (loaded before
+    # torch, it bound the system copy and gemm_create returned GEMM_ERR_HIP)
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.gemm_create.argtypes = [ctypes.POINTER(vp)]

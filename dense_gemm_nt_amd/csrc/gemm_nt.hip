@@ -274,8 +274,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     // (tile, k-slab) units instead, each tile it touches giving one partial
     // (a 256 KB slot).  Only for runs of at least 32 k-slabs: each segment
     // refills the pipeline and writes a whole partial tile, which shorter runs
-    // do not pay back.  `streamk`: 0 never (callers without the persistent
-    // ping-pong kernel), 1 by this rule, 2 whenever the tile is the ping-pong one.
+    // do not pay back.  `streamk`: 0 never, 1 by this rule, 2 whenever the tile
+    // is the ping-pong one.  Handles default to 0: on MI355X stream-K measured
+    // slower than the plain plan on every shape tried (3000 x 3000 x 5000: 125
+    // vs 118 us; 2304 x 2304 x 8192: 128 vs 91; 3000 x 3000 x 1536: 67 vs 45).
+    // These launches are bound by the MFMA work at a power-limited clock: the
+    // compute units a plain plan leaves idle let the busy ones clock higher, so
+    // spreading the same work over all of them gains little, and the partial
+    // slots and their reduction add traffic and a second kernel.
     if (streamk > 0 && cfg == CFG_PP2_256x256 && force_splits <= 0 && tiles > 0 && p.k_tiles > 0) {
         const int64_t T = tiles * p.k_tiles;
         const int64_t G = std::min<int64_t>(kNumCUs, T);
@@ -298,6 +304,16 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
 
 }  // namespace
 
+// Plans of a handle's recent shapes: the planner's result depends only on the
+// problem and on the handle's fixed settings, so a repeated shape skips it.
+struct PlanCacheEntry {
+    int64_t M, N, K;
+    int cfg, streamk, inreduce;   // make_plan's per-call arguments
+    int valid;
+    Plan plan;
+};
+constexpr int kPlanCacheSize = 16;
+
 struct gemm_handle_s {
     int device;
     float *partials;
@@ -306,7 +322,7 @@ struct gemm_handle_s {
     int force_splits;
     int persistent;    // GEMM_PERSIST=1: ping-pong tiles run by 256 persistent blocks
     int inreduce;      // GEMM_INREDUCE: 1 (default) two K splits reduced in the kernel, 0 never
-    int streamk;       // GEMM_STREAMK: 0 off, 1 by the plan rule (default), 2 whenever
+    int streamk;       // GEMM_STREAMK: 0 off (default), 1 by the plan rule, 2 whenever
                        // the ping-pong tile is planned
     int log;
     // grouped launches: pinned staging of the problem list and an event that
@@ -315,7 +331,29 @@ struct gemm_handle_s {
     int64_t staging_bytes;
     hipEvent_t staged;
     int staged_pending;
+    PlanCacheEntry plans[kPlanCacheSize];
+    int plan_next;
 };
+
+namespace {
+
+// make_plan with the handle's workspace and split settings, through its cache
+// (the handle is used by one caller at a time, so the cache takes no lock).
+Plan handle_plan(gemm_handle_s *h, int64_t M, int64_t N, int64_t K, int cfg, int streamk,
+                 int inreduce)
+{
+    for (const PlanCacheEntry &e : h->plans)
+        if (e.valid && e.M == M && e.N == N && e.K == K && e.cfg == cfg && e.streamk == streamk &&
+            e.inreduce == inreduce)
+            return e.plan;
+    PlanCacheEntry &e = h->plans[h->plan_next];
+    h->plan_next = (h->plan_next + 1) % kPlanCacheSize;
+    e = PlanCacheEntry{M, N, K, cfg, streamk, inreduce, 1,
+                       make_plan(M, N, K, h->ws_bytes, cfg, h->force_splits, streamk, inreduce)};
+    return e.plan;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -385,7 +423,7 @@ gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
         return GEMM_ERR_INVALID_ARG;
     if (M >= INT32_MAX || N >= INT32_MAX || K >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
-    const Plan p = make_plan(M, N, K, kDefaultWorkspaceMB << 20, -1, -1, 1);
+    const Plan p = make_plan(M, N, K, kDefaultWorkspaceMB << 20, -1, -1, 0);
     const Config &c = kConfigs[p.cfg];
     out->block_m = c.bm;
     out->block_n = c.bn;
@@ -428,7 +466,7 @@ gemm_status_t gemm_create(gemm_handle_t *out)
         h->force_splits = atoi(e);
     if (const char *e = getenv("GEMM_PERSIST"))
         h->persistent = atoi(e) != 0;
-    h->streamk = 1;
+    h->streamk = 0;
     if (const char *e = getenv("GEMM_STREAMK"))
         h->streamk = atoi(e);
     if (const char *e = getenv("GEMM_LOG"))
@@ -627,8 +665,8 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     const bool nt = !am && !bnm;
     if (!nt && h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
         return GEMM_ERR_UNSUPPORTED;
-    const Plan p = make_plan(M, N, K, h->ws_bytes, nt ? h->force_cfg : CFG_PP2_256x256,
-                             h->force_splits, nt ? h->streamk : 0, h->inreduce && !h->persistent);
+    const Plan p = handle_plan(h, M, N, K, nt ? h->force_cfg : CFG_PP2_256x256,
+                               nt ? h->streamk : 0, h->inreduce && !h->persistent);
     KernelArgs a{};
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);
@@ -691,9 +729,10 @@ gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C, int64_t M,
     void *ptr = nullptr;
     if ((st = noalloc_scratch(&ptr)) != GEMM_OK)
         return st;
-    // gemm_run's plan with its partials bounded by the scratch: K splits or
-    // stream-K that would need more take fewer splits or the split plan
-    const Plan p = make_plan(M, N, K, GEMM_NOALLOC_SCRATCH_BYTES, -1, -1, 1);
+    // gemm_run's default plan: its partials never need more than the scratch
+    // (at most 256 tiles x splits of 256 x 256 FP32 values), and the planner's
+    // bound would take fewer splits if they did
+    const Plan p = make_plan(M, N, K, GEMM_NOALLOC_SCRATCH_BYTES, -1, -1, 0);
     if ((p.splits > 1 || p.stream) && p.ws_bytes > GEMM_NOALLOC_SCRATCH_BYTES)
         return GEMM_ERR_UNSUPPORTED;
     KernelArgs a{};
@@ -1001,7 +1040,7 @@ gemm_status_t gemm_run_fp8(gemm_handle_t h, int a_dtype, int b_dtype, const void
     if (h->force_cfg >= 0 && h->force_cfg != CFG_PP2_256x256)
         return GEMM_ERR_UNSUPPORTED;
     // A slab is 128 bytes of each row: 128 FP8 values, planned as 64 16-bit ones
-    const Plan p = make_plan(M, N, K / 2, h->ws_bytes, CFG_PP2_256x256, h->force_splits, 0, h->inreduce);
+    const Plan p = handle_plan(h, M, N, K / 2, CFG_PP2_256x256, 0, h->inreduce);
     KernelArgs a{};
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);

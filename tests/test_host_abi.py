@@ -137,10 +137,10 @@ def test_plan_regimes(g):
     # decode with few tiles splits K to cover the compute units
     p = g.gemm_plan(256, 8192, 8192)
     assert (p["splits"] > 1 or p["streamk"]) and p["workgroups"] >= 128
-    # few big tiles with a long K: stream-K over all 256 compute units; with a
-    # short K (runs under 32 k-slabs) or a well-filled split plan, not
+    # few big tiles with a long K: the ping-pong tiles alone (stream-K is opt-in)
     p = g.gemm_plan(3000, 3000, 5000)
-    assert p["streamk"] == 1 and p["workgroups"] == 256 and p["splits"] == 1
+    assert p["streamk"] == 0 and p["workgroups"] == 144 and p["splits"] == 1
+    assert p["name"] == "256x256x64_w8_pp2"
     assert g.gemm_plan(3000, 3000, 3000)["streamk"] == 0
     assert g.gemm_plan(256, 28672, 8192)["streamk"] == 0
     assert g.gemm_plan(4096, 4096, 4096)["streamk"] == 0

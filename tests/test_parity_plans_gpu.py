@@ -63,3 +63,21 @@ def test_default_plan_every_element(i):
 def test_the_draw_reaches_each_tile_family():
     names = {gemm_plan(M, N, K)["name"] for M, N, K in SHAPES}
     assert {"32x128x64_w4_s6", "128x128x64_w4_s4", "128x128x64_w4_s2", "256x256x64_w8_pp2"} <= names, names
+
+
+def test_plan_cache_over_many_shapes():
+    # one handle through all the planner regimes above (more shapes than its
+    # plan cache holds), then the first shapes again: every call gives the bits
+    # a fresh handle gives (same plan, same summation order)
+    h = new_handle()
+    order = list(range(len(SHAPES))) + [0, 1, 2, len(SHAPES) - 1]
+    for n, i in enumerate(order):
+        M, N, K = SHAPES[i]
+        say("case plan cache call %d: M=%d N=%d K=%d" % (n, M, N, K))
+        A, B = make_operands(M, N, K, "bf16", "uniform", seed=100 + n)
+        C = run_gpu(h, A, B, K, "bf16", "fp32")
+        h2 = new_handle()
+        R = run_gpu(h2, A, B, K, "bf16", "fp32")
+        h2.close()
+        assert np.array_equal(C, R), (M, N, K)
+    h.close()

@@ -9,6 +9,8 @@ tiles included, so that many partials meet in one tile.  Small-integer inputs
 make every partial sum exact: those comparisons are bitwise.  The fused epilogue
 runs in the reduction kernel and is checked against oracle.epilogue.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,7 @@ from oracle import epilogue as oepi
 from dense_gemm_nt_amd import _lib, gemm_plan
 from gemm_inputs import make_operands
 from tests.gpu_util import CODE, TORCH_DT, compare_full, new_handle, run_gpu, say
-from tests.tolerance import check_epilogue
+from tests.tolerance import check, check_epilogue
 
 pytestmark = pytest.mark.gpu
 
@@ -91,8 +93,23 @@ def test_streamk_fused_epilogue(alpha, beta, along, act):
     check_epilogue(D, Dr, aS, t, "bf16", "stream-K epilogue")
 
 
-def test_streamk_is_planned_for_few_tiles_with_long_k():
-    # (3000, 3000, 5000): 144 tiles, runs of ~44 k-slabs; the workload parity
-    # tests run this shape through the default plan
-    p = gemm_plan(3000, 3000, 5000, _lib.GEMM_FP16, _lib.GEMM_FP32)
-    assert p["streamk"] == 1 and p["workgroups"] == 256
+def test_streamk_rule_is_opt_in(capfd):
+    # the default plan never takes stream-K; GEMM_STREAMK=1 applies the rule,
+    # which picks it for (3000, 3000, 5000): 144 tiles, runs of ~44 k-slabs
+    M, N, K = 3000, 3000, 5000
+    p = gemm_plan(M, N, K, _lib.GEMM_FP16, _lib.GEMM_FP32)
+    assert p["streamk"] == 0
+    say("case stream-K by the plan rule M=%d N=%d K=%d fp16->fp32" % (M, N, K))
+    os.environ["GEMM_LOG"] = "1"
+    try:
+        h = new_handle(streamk=1)
+    finally:
+        os.environ.pop("GEMM_LOG", None)
+    A, B = make_operands(M, N, K, "fp16", "uniform", seed=5)
+    capfd.readouterr()
+    C = run_gpu(h, A, B, K, "fp16", "fp32")
+    err = capfd.readouterr().err
+    h.close()
+    assert "stream-K" in err and "grid=256" in err, err
+    Cr, S = oracle.gemm_nt(A, B, K=K, in_dtype="fp16")
+    check(C, Cr, S, "fp32", "stream-K by the plan rule")
