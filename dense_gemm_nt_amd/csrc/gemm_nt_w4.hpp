@@ -1,46 +1,45 @@
-// gemm_nt_w4.hpp -- four-wave 256x256 NT GEMM tile for gfx950: one wave per
-// SIMD, each wave owning a 128 x 128 block of C whose FP32 accumulators fill
-// the accumulation registers, over an LDS ring of five 32 KB units.
+// gemm_nt_w4.hpp -- four-wave 256 x BN NT GEMM tile for gfx950 (BN = 128):
+// one wave per SIMD, each wave owning a 128 x (BN / 2)
+// block of C whose FP32 accumulators sit in the accumulation registers, over an
+// LDS ring of two 32 KB A units and NUB B units of BN x 128 bytes.
 //
-// Why this shape.  A 32x32x16 MFMA step of a wave with a WM x WN block reads
-// (WM + WN) / 32 operand fragments of 1 KB from LDS for WM WN / 1024 MFMAs.  At
-// 128 x 128 that is 8 fragment reads per 16 MFMAs; at 64 x 128 (the eight-wave
-// ping-pong tile) 6 per 8.  One third less LDS read traffic per MFMA leaves
-// the LDS with headroom under the matrix cores and spends less energy per
-// FLOP on a part whose clock the power limit sets.  A wave needs 256 FP32
-// accumulators per lane for that block, which only one wave per SIMD has room
-// for (512 registers per lane); so the wave itself overlaps everything: its
+// Why this shape.  Decode batches (M = 256) have few tiles along N, and the
+// 256 x 256 ping-pong tile needs many K splits to occupy the machine, each
+// split writing an FP32 copy of its tile.  A 256 x 128 tile gives twice the
+// tiles, so half the splits for the same occupancy ("A Blackwell GEMM by Hand
+// in CuTe DSL", section 9: decode, split-K).  A wave's block needs (FM * FN)
+// x 16 FP32 accumulators per lane; with one wave per SIMD there are 512
+// registers per lane for them, and the wave itself overlaps everything: its
 // MFMAs run while it issues the fragment reads of the next k-step and the
-// direct-to-LDS loads of later slabs ("A Blackwell GEMM by Hand in CuTe DSL",
-// section 3: the copies of later stages overlap the MMAs of the current one;
-// "Matmul on sm_120", kernel 3: the shared-memory and register pipelines
-// nested).
+// direct-to-LDS loads of later slabs (section 3: the copies of later stages
+// overlap the MMAs of the current one; "Matmul on sm_120", kernel 3: the
+// shared-memory and register pipelines nested).
 //
-// Ring.  A slab is 64 deep: 256 rows of 128 bytes per operand, one 32 KB unit
-// each.  Every load instruction fetches whole 128-byte rows (8 rows per 1 KB
-// wave-wide load), so each request is one cache line.  The 160 KB of LDS hold
-// five units: A(i) lives in unit i mod 2, B(i) in unit 2 + i mod 3.  The
-// barrier of slab i frees both of its units; A(i + 2) and B(i + 3) go into
-// them.  So B, the operand a decode-shaped call streams from HBM, is issued
-// about five k-steps before the barrier that needs it, and A about three
-// (section 7: enough stages in flight for the load latency).  Logical 16-byte
-// chunk c of row r sits at physical chunk c ^ key(r) (section 6: the XOR
-// swizzle; row_key), and the direct-to-LDS load, which writes 1 KB
-// lane-contiguously, applies it on the global side: the lane that fills
-// physical chunk p of row r fetches logical chunk p ^ key(r).
+// Ring.  A slab is 64 deep: 256 rows of 128 bytes of A (one 32 KB unit) and
+// BN rows of B (one B unit).  Every load instruction fetches whole 128-byte
+// rows (8 rows per 1 KB wave-wide load), so each request is one cache line.
+// A(i) lives in A unit i mod 2, B(i) in B unit i mod NUB (NUB = 6 at BN =
+// 128: 64 + 96 KB).  The barrier of slab i frees both of its units; A(i + 2)
+// and B(i + NUB) go into them.  So B, the operand a decode-shaped call streams
+// from HBM, is issued several slabs before the barrier that needs it, and A
+// (which such a call reads from L2) one slab ahead (section 7: enough stages
+// in flight for the load latency).  Logical 16-byte chunk c of row r sits at
+// physical chunk c ^ key(r) (section 6: the XOR swizzle; row_key), and the
+// direct-to-LDS load, which writes 1 KB lane-contiguously, applies it on the
+// global side: the lane that fills physical chunk p of row r fetches logical
+// chunk p ^ key(r).
 //
 // Hand-off (sections 2-3: full/empty barriers).  One workgroup barrier per
-// slab, before its last k-step: every wave then holds the slab's last
-// fragments in registers (the slab's units may be refilled) and has seen its
-// own loads of the next slab land (vmcnt); after it, the next slab's first
-// fragments are read under the last k-step's MFMAs.  Each k-step issues four
-// of a wave's sixteen loads per slab beside its MFMAs, so the four waves'
-// vector-memory issue is spread over the slab.
+// slab, before the last MFMAs of its third k-step: every wave then holds the
+// slab's last fragments in registers (the slab's units may be refilled) and
+// has seen its own loads of the next slab land (vmcnt); after it, the next
+// slab's first fragments are read under the last k-step's MFMAs.  The loads
+// of a slab are spread over its k-steps, beside the MFMAs.
 //
-// Output: wave w owns rows [128 (w / 2), +128) and columns [128 (w % 2), +128)
-// as 4 x 4 blocks of 32 x 32.  The B fragment is the MFMA's first operand, so
-// accumulator register 4q + e of lane l in block (fn, fm) holds
-// C[32 fm + l % 32][32 fn + 8 q + 4 (l / 32) + e].  Requires K % 8 == 0.
+// Output: wave w owns rows [128 (w / 2), +128) and columns [(BN / 2) (w % 2),
+// +BN / 2) as 4 x (BN / 64) blocks of 32 x 32.  The B fragment is the MFMA's
+// first operand, so accumulator register 4q + e of lane l in block (fn, fm)
+// holds C[32 fm + l % 32][32 fn + 8 q + 4 (l / 32) + e].  Requires K % 8 == 0.
 #pragma once
 
 #include <type_traits>
@@ -180,13 +179,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     constexpr int PITCH = 128;                // bytes per LDS row (64 16-bit values)
     constexpr int CH = 8;                     // 16-byte chunks per row
     constexpr int UA = BM * PITCH;            // A of one slab, 32 KB
-    constexpr int UBB = BN * PITCH;           // B of one slab, 32 or 16 KB
-    constexpr int NUB = (160 * 1024 - 2 * UA) / UBB;   // B units: 3 or 6
+    constexpr int UBB = BN * PITCH;           // B of one slab, 16 KB
+    constexpr int NUB = (160 * 1024 - 2 * UA) / UBB;   // B units: 6
     constexpr int FM = 4, FN = BN / 64;       // wave block 128 x (BN / 2)
     constexpr int LA = BM / 32, LB = BN / 32; // loads per wave and slab
     constexpr int MF = FN * FM;               // MFMAs per k-step
     constexpr int NR = FM + FN;               // fragment reads per k-step
-    static_assert(BN == 256 || BN == 128, "tile");
+    static_assert(BN == 128, "the 256 x 128 tile is the instantiated and tested one");
     static_assert(2 * UA + NUB * UBB <= 160 * 1024, "LDS budget");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * UA + NUB * UBB];
