@@ -100,30 +100,24 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
     const uint32_t ldsA = lds_base;
     const uint32_t ldsB = lds_base + STAGES * A_BYTES;
 
-    // One stage's loads; B's take the non-temporal policy when B is streamed
-    // (one branch per stage picks the copy with that policy).
-    auto issue = [&](int kt, int s) {
+    // Load j (0 .. NL-1: A's loads, then B's) of slab kt into stage s; B's
+    // take the non-temporal policy `nt` when B is streamed (the policy is an
+    // immediate of the instruction, so the main loop exists once per policy).
+    constexpr int NL = A_LOADS + B_LOADS;
+    auto issue_one = [&](int kt, int s, int j, auto nt) {
         const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * 2);
         const bool kin = lc * 8 < p.K - kt * BK;
-        auto loads = [&](auto nt) {
-#pragma unroll
-            for (int j = 0; j < A_LOADS; ++j) {
-                const uint32_t r = (uint32_t)min(lrow0 + j * RSTEP, rows_a - 1);
-                const uint32_t v = kin ? r * lda2 + (uint32_t)lc * 16u : kOutOfRange;
-                load_lds16(rsA, v, koff, ldsA + s * A_BYTES + (j * NWAVES + wave) * 1024);
-            }
-#pragma unroll
-            for (int j = 0; j < B_LOADS; ++j) {
-                const uint32_t r = (uint32_t)min(lrow0 + j * RSTEP, rows_b - 1);
-                const uint32_t v = kin ? r * ldb2 + (uint32_t)lc * 16u : kOutOfRange;
-                load_lds16_policy<decltype(nt)::value>(rsB, v, koff,
-                                                       ldsB + s * B_BYTES + (j * NWAVES + wave) * 1024);
-            }
-        };
-        if (p.nt_b)
-            loads(std::true_type{});
-        else
-            loads(std::false_type{});
+        if (j < A_LOADS) {
+            const uint32_t r = (uint32_t)min(lrow0 + j * RSTEP, rows_a - 1);
+            const uint32_t v = kin ? r * lda2 + (uint32_t)lc * 16u : kOutOfRange;
+            load_lds16(rsA, v, koff, ldsA + s * A_BYTES + (j * NWAVES + wave) * 1024);
+        } else {
+            const int jb = j - A_LOADS;
+            const uint32_t r = (uint32_t)min(lrow0 + jb * RSTEP, rows_b - 1);
+            const uint32_t v = kin ? r * ldb2 + (uint32_t)lc * 16u : kOutOfRange;
+            load_lds16_policy<decltype(nt)::value>(rsB, v, koff,
+                                                   ldsB + s * B_BYTES + (jb * NWAVES + wave) * 1024);
+        }
     };
 
     // Per-lane LDS read offsets of the MFMA operand chunk for each k16 step.
@@ -145,8 +139,12 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
                 acc[i][j][e] = 0.0f;
 
     // One BK slab from LDS: KSTEPS k16 steps of FN x FM MFMAs.  The operand
-    // chunks of step ks+1 are read while the MFMAs of step ks run.
-    auto compute_slab = [&](const uint8_t *sa, const uint8_t *sb, int kvalid) {
+    // chunks of step ks+1 are read while the MFMAs of step ks run, and
+    // `load(j)` (j = 0 .. NL-1, the loads of a later slab) is called between
+    // the MFMAs, spread over the k-steps, so that the loads' issue, which the
+    // vector memory unit accepts at about one 1 KB load per 25 cycles, can run
+    // beside the matrix cores instead of ahead of them.
+    auto compute_slab = [&](const uint8_t *sa, const uint8_t *sb, int kvalid, auto load) {
         u32x4 af[2][FM], bf[2][FN];
         auto fetch = [&](int ks, int slot) {
 #pragma unroll
@@ -171,35 +169,67 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
                 for (int fn = 0; fn < FN; ++fn)
                     bf[cur][fn] = mask_chunk(bf[cur][fn], nvalid);
             }
+            // this k-step's share of the loads, one after each of its first MFMAs
+            constexpr int PER = (NL + KSTEPS - 1) / KSTEPS;
+            int t = 0;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
+                for (int fm = 0; fm < FM; ++fm) {
                     acc[fn][fm] = mfma32x32x16<IN>(bf[cur][fn], af[cur][fm], acc[fn][fm]);
+                    if (t < PER && ks * PER + t < NL)
+                        load(ks * PER + t);
+                    ++t;
+                }
+            // (a k-step with fewer MFMAs than its share issues the rest here)
+#pragma unroll
+            for (; t < PER; ++t)
+                if (ks * PER + t < NL)
+                    load(ks * PER + t);
         }
     };
 
     const int nkt = kt_end - kt_begin;
-    if (nkt > 0) {
-        // Prologue: fill STAGES-1 slabs.
+    auto main_loop = [&](auto nt) {
+        // Where the next slab's loads go.  With B streamed from HBM (the
+        // non-temporal policy: one or two tile rows, small M) or a two-stage
+        // ring (one slab in flight): all at once after the slab's barrier,
+        // which gives them the whole slab to land.  Otherwise: spread between
+        // the MFMAs, where their issue no longer holds the matrix cores back
+        // (4-16% on 1024 x 4096 x 2048, 1536^3, 2048^3; 1-4% slower on the
+        // streamed small-M shapes).
+        constexpr bool EARLY = decltype(nt)::value || STAGES <= 2;
+        // Spread loads sit inside the slab's code with no branch around them,
+        // so every iteration issues NL loads per wave: slabs past the split's
+        // last one re-read that slab into a stage no later slab reads.  The
+        // wait then has one count: slab i has landed for this wave once at
+        // most the (STAGES - 2) NL loads of the slabs after it are in flight.
+        // Issued at once, the loads past the end are skipped instead, and the
+        // last iterations wait for everything.
+        auto slab_kt = [&](int i) { return kt_begin + min(i, nkt - 1); };
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
-            if (s < nkt)
-                issue(kt_begin + s, s);
+            if (!EARLY || s < nkt)
+#pragma unroll
+                for (int j = 0; j < NL; ++j)
+                    issue_one(slab_kt(s), s, j, nt);
 
         for (int i = 0; i < nkt; ++i) {
             const int s = i % STAGES;
-            // Slab i landed for this wave once at most (STAGES-2) newer slabs are in flight.
-            if (i + STAGES - 2 < nkt) {
-                static_assert((STAGES - 2) * (A_LOADS + B_LOADS) <= 63, "vmcnt range");
-                wait_vmcnt<(STAGES - 2) * (A_LOADS + B_LOADS)>();
-            } else {
+            static_assert((STAGES - 2) * NL <= 63, "vmcnt range");
+            if (EARLY && i + STAGES - 2 >= nkt)
                 wait_vmcnt<0>();
-            }
+            else
+                wait_vmcnt<(STAGES - 2) * NL>();
             wait_lgkmcnt0();
             wg_barrier();
-            if (i + STAGES - 1 < nkt)
-                issue(kt_begin + i + STAGES - 1, (i + STAGES - 1) % STAGES);
+            const int kt_next = slab_kt(i + STAGES - 1), s_next = (i + STAGES - 1) % STAGES;
+            if constexpr (EARLY) {
+                if (i + STAGES - 1 < nkt)
+#pragma unroll
+                    for (int j = 0; j < NL; ++j)
+                        issue_one(kt_next, s_next, j, nt);
+            }
 
             const uint8_t *sa = smem + s * A_BYTES + wave_m * WTM * PITCH;
             const uint8_t *sb = smem + STAGES * A_BYTES + s * B_BYTES + wave_n * WTN * PITCH;
@@ -207,8 +237,20 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
             // When K is not a multiple of 8 the slab holding column K-1 also holds
             // columns past K in its last chunk (the row's padding); KMASK builds
             // zero those in registers.  Without it K % 8 == 0 is required.
-            compute_slab(sa, sb, p.K - kt * BK);
+            compute_slab(sa, sb, p.K - kt * BK, [&](int j) {
+                if constexpr (!EARLY)
+                    issue_one(kt_next, s_next, j, nt);
+            });
         }
+        // the re-read loads of the last iterations may still be in flight
+        if constexpr (!EARLY)
+            wait_vmcnt<0>();
+    };
+    if (nkt > 0) {
+        if (p.nt_b)
+            main_loop(std::true_type{});
+        else
+            main_loop(std::false_type{});
     }
 
     // Epilogue without a fused epilogue: each wave's block through its share of

@@ -192,7 +192,7 @@ def _expected_mfma(name):
     fam = _family(name)
     if fam == "gemm_nt_kernel":
         bm, bn, bk, wm, wn = a[:5]
-        return (bm // wm // 32) * (bn // wn // 32) * (bk // 16)          # one loop
+        return (bm // wm // 32) * (bn // wn // 32) * (bk // 16) * 2      # one loop per B policy
     if fam == "gemm_nt_pp2":
         in_t, sc = a[0], a[4]
         per_slab = 2 * 4 * (4 if in_t < 2 else 2)     # 64 x 128 per wave; x16 or x64 k-steps
