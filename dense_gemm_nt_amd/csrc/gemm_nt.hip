@@ -154,16 +154,16 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         // Decode batches: the whole of M in one 256-row tile of the ping-pong
         // kernel (A stays in L2, every compute unit streams its own 256-row
         // panel of B), and split-K below to bring the grid up to the machine.
-        // When that tile would need more than four K splits with K up to 16384
-        // (few N tiles: 256 x 10240 x 8192, 256 x 8192 x 8192), the four-wave
-        // 256 x 128 tile fills the machine with half as many splits, i.e. half
-        // the FP32 partial traffic (measured 67.6 -> 59.5 us at 256 x 10240 x 8192,
-        // even at 256 x 8192 x 8192; slower at 256 x 8192 x 28672, whose long K
-        // the ping-pong tile splits eight ways, and at 256 x 28672 x 8192).
+        // When that tile would need more than four K splits (few N tiles:
+        // 256 x 10240 x 8192, 256 x 8192 x 8192, 256 x 8192 x 28672), the
+        // four-wave 256 x 128 tile fills the machine with half as many splits,
+        // i.e. half the FP32 partial traffic (interleaved medians: 59.5 -> 56.6,
+        // 53.0 -> 50.0, 126.2 -> 123.0 us; with two splits, at 256 x 28672 x
+        // 8192, the ping-pong tile stays faster: 122.6 against 126.1 us).
         cfg = CFG_PP2_256x256;
         const int64_t t256 = cdiv(N, 256), kt64 = cdiv(K, 64);
         const int64_t s256 = std::min<int64_t>(kNumCUs / std::max<int64_t>(1, t256), kt64 / 20);
-        if (t256 < kNumCUs && s256 > 4 && K <= 16384)
+        if (t256 < kNumCUs && s256 > 4)
             cfg = CFG_W4_256x128;
     } else {
         // The 256x256 ping-pong tile when its blocks fill at least half the
@@ -274,14 +274,13 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     // (tile, k-slab) units instead, each tile it touches giving one partial
     // (a 256 KB slot).  Only for runs of at least 32 k-slabs: each segment
     // refills the pipeline and writes a whole partial tile, which shorter runs
-    // do not pay back.  `streamk`: 0 never, 1 by this rule, 2 whenever the tile
-    // is the ping-pong one.  Handles default to 0: on MI355X stream-K measured
-    // slower than the plain plan on every shape tried (3000 x 3000 x 5000: 125
-    // vs 118 us; 2304 x 2304 x 8192: 128 vs 91; 3000 x 3000 x 1536: 67 vs 45).
-    // These launches are bound by the MFMA work at a power-limited clock: the
-    // compute units a plain plan leaves idle let the busy ones clock higher, so
-    // spreading the same work over all of them gains little, and the partial
-    // slots and their reduction add traffic and a second kernel.
+    // do not pay back.  `streamk`: 0 never, 1 by this rule (the default), 2
+    // whenever the tile is the ping-pong one.  Interleaved medians on operands
+    // read cold: 3000 x 3000 x 5000 (144 tiles) 126 us against 141 without;
+    // 2304 x 2304 x 8192 (three splits fill the machine) 130 against 88;
+    // 3000 x 3000 x 1536 (runs of 13 slabs) 70 against 50.  With operands
+    // resident in the memory-side cache the first one reverses (125 against
+    // 118): stream-K pays where the idle compute units would add HBM streams.
     if (streamk > 0 && cfg == CFG_PP2_256x256 && force_splits <= 0 && tiles > 0 && p.k_tiles > 0) {
         const int64_t T = tiles * p.k_tiles;
         const int64_t G = std::min<int64_t>(kNumCUs, T);
@@ -322,7 +321,7 @@ struct gemm_handle_s {
     int force_splits;
     int persistent;    // GEMM_PERSIST=1: ping-pong tiles run by 256 persistent blocks
     int inreduce;      // GEMM_INREDUCE: 1 (default) two K splits reduced in the kernel, 0 never
-    int streamk;       // GEMM_STREAMK: 0 off (default), 1 by the plan rule, 2 whenever
+    int streamk;       // GEMM_STREAMK: 0 off, 1 by the plan rule (default), 2 whenever
                        // the ping-pong tile is planned
     int log;
     // grouped launches: pinned staging of the problem list and an event that
@@ -423,7 +422,7 @@ gemm_status_t gemm_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
         return GEMM_ERR_INVALID_ARG;
     if (M >= INT32_MAX || N >= INT32_MAX || K >= INT32_MAX)
         return GEMM_ERR_UNSUPPORTED;
-    const Plan p = make_plan(M, N, K, kDefaultWorkspaceMB << 20, -1, -1, 0);
+    const Plan p = make_plan(M, N, K, kDefaultWorkspaceMB << 20, -1, -1, 1);
     const Config &c = kConfigs[p.cfg];
     out->block_m = c.bm;
     out->block_n = c.bn;
@@ -466,7 +465,7 @@ gemm_status_t gemm_create(gemm_handle_t *out)
         h->force_splits = atoi(e);
     if (const char *e = getenv("GEMM_PERSIST"))
         h->persistent = atoi(e) != 0;
-    h->streamk = 0;
+    h->streamk = 1;
     if (const char *e = getenv("GEMM_STREAMK"))
         h->streamk = atoi(e);
     if (const char *e = getenv("GEMM_LOG"))
@@ -729,10 +728,10 @@ gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C, int64_t M,
     void *ptr = nullptr;
     if ((st = noalloc_scratch(&ptr)) != GEMM_OK)
         return st;
-    // gemm_run's default plan: its partials never need more than the scratch
-    // (at most 256 tiles x splits of 256 x 256 FP32 values), and the planner's
-    // bound would take fewer splits if they did
-    const Plan p = make_plan(M, N, K, GEMM_NOALLOC_SCRATCH_BYTES, -1, -1, 0);
+    // gemm_run's plan with its partials bounded by the scratch: a stream-K plan
+    // that would need more takes the split plan (K split partials never need
+    // more than 64 MiB: at most 256 tiles x splits of 256 x 256 FP32 values)
+    const Plan p = make_plan(M, N, K, GEMM_NOALLOC_SCRATCH_BYTES, -1, -1, 1);
     if ((p.splits > 1 || p.stream) && p.ws_bytes > GEMM_NOALLOC_SCRATCH_BYTES)
         return GEMM_ERR_UNSUPPORTED;
     KernelArgs a{};

@@ -1,7 +1,7 @@
 // gemm_nt_w4.hpp -- four-wave 256 x BN NT GEMM tile for gfx950 (BN = 128):
-// one wave per SIMD, each wave owning a 128 x (BN / 2)
-// block of C whose FP32 accumulators sit in the accumulation registers, over an
-// LDS ring of two 32 KB A units and NUB B units of BN x 128 bytes.
+// one wave per SIMD, each wave owning a 128 x (BN / 2) block of C whose FP32
+// accumulators sit in the accumulation registers, over an LDS ring of three
+// 32 KB A units and four 16 KB B units.
 //
 // Why this shape.  Decode batches (M = 256) have few tiles along N, and the
 // 256 x 256 ping-pong tile needs many K splits to occupy the machine, each
@@ -16,18 +16,19 @@
 // shared-memory and register pipelines nested).
 //
 // Ring.  A slab is 64 deep: 256 rows of 128 bytes of A (one 32 KB unit) and
-// BN rows of B (one B unit).  Every load instruction fetches whole 128-byte
-// rows (8 rows per 1 KB wave-wide load), so each request is one cache line.
-// A(i) lives in A unit i mod 2, B(i) in B unit i mod NUB (NUB = 6 at BN =
-// 128: 64 + 96 KB).  The barrier of slab i frees both of its units; A(i + 2)
-// and B(i + NUB) go into them.  So B, the operand a decode-shaped call streams
-// from HBM, is issued several slabs before the barrier that needs it, and A
-// (which such a call reads from L2) one slab ahead (section 7: enough stages
-// in flight for the load latency).  Logical 16-byte chunk c of row r sits at
-// physical chunk c ^ key(r) (section 6: the XOR swizzle; row_key), and the
-// direct-to-LDS load, which writes 1 KB lane-contiguously, applies it on the
-// global side: the lane that fills physical chunk p of row r fetches logical
-// chunk p ^ key(r).
+// BN rows of B (one 16 KB unit).  Every load instruction fetches whole
+// 128-byte rows (8 rows per 1 KB wave-wide load), so each request is one
+// cache line.  A(i) lives in A unit i mod 3, B(i) in B unit i mod 4 (96 + 64
+// KB).  The barrier of slab i frees both of its units; A(i + 3) and B(i + 4)
+// go into them.  Both operands are issued about two slabs before the barrier
+// that needs them: B, which a decode-shaped call streams from HBM, and A,
+// which it re-reads from L2 for every tile at twice B's bytes (section 7:
+// enough stages in flight for the load latency; two A units, one slab ahead,
+// measured 3-5% slower on the decode shapes).  Logical 16-byte chunk c of row
+// r sits at physical chunk c ^ key(r) (section 6: the XOR swizzle; row_key),
+// and the direct-to-LDS load, which writes 1 KB lane-contiguously, applies it
+// on the global side: the lane that fills physical chunk p of row r fetches
+// logical chunk p ^ key(r).
 //
 // Hand-off (sections 2-3: full/empty barriers).  One workgroup barrier per
 // slab, before the last MFMAs of its third k-step: every wave then holds the
@@ -180,15 +181,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     constexpr int CH = 8;                     // 16-byte chunks per row
     constexpr int UA = BM * PITCH;            // A of one slab, 32 KB
     constexpr int UBB = BN * PITCH;           // B of one slab, 16 KB
-    constexpr int NUB = (160 * 1024 - 2 * UA) / UBB;   // B units: 6
+    constexpr int NUA = 3;                    // A units
+    constexpr int NUB = (160 * 1024 - NUA * UA) / UBB;   // B units: 4
     constexpr int FM = 4, FN = BN / 64;       // wave block 128 x (BN / 2)
     constexpr int LA = BM / 32, LB = BN / 32; // loads per wave and slab
     constexpr int MF = FN * FM;               // MFMAs per k-step
     constexpr int NR = FM + FN;               // fragment reads per k-step
     static_assert(BN == 128, "the 256 x 128 tile is the instantiated and tested one");
-    static_assert(2 * UA + NUB * UBB <= 160 * 1024, "LDS budget");
+    static_assert(NUA == 3 && NUB == 4, "the load schedule below is written for 3 A and 4 B units");
+    static_assert(NUA * UA + NUB * UBB <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * UA + NUB * UBB];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NUA * UA + NUB * UBB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
             load_lds16(rsA, v, kb, lds0 + (uint32_t)(u * UA + (row - lr) * PITCH));
         } else {
             const uint32_t v = kin ? (uint32_t)min(row, rows_b - 1) * ldb2 + (uint32_t)lc * 16u : kOutOfRange;
-            load_lds16_policy<decltype(nt)::value>(rsB, v, kb, lds0 + (uint32_t)(2 * UA + u * UBB + (row - lr) * PITCH));
+            load_lds16_policy<decltype(nt)::value>(rsB, v, kb, lds0 + (uint32_t)(NUA * UA + u * UBB + (row - lr) * PITCH));
         }
     };
 
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
                 *reinterpret_cast<const u32x4 *>(smem + ua * UA + off + (wm * 128 + (n - 1) * 32) * PITCH);
         else {
             const int f = n == 0 ? 0 : n - FM;
-            fb[buf][f] = *reinterpret_cast<const u32x4 *>(smem + 2 * UA + ub * UBB + off +
+            fb[buf][f] = *reinterpret_cast<const u32x4 *>(smem + NUA * UA + ub * UBB + off +
                                                           (wn * (BN / 2) + f * 32) * PITCH);
         }
     };
@@ -285,27 +288,42 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     // beside the following ones; the slab's barrier comes before the last two
     // MFMAs of k-step 2, which keep the matrix core busy while the waves meet.
     //
-    // Loads: A(i) lives in A unit i mod 2, B(i) in B unit i mod NUB.  The
-    // barrier of slab i frees both units of slab i; A(i + 2) goes into its A
-    // unit in k-step 3 of slab i and k-step 0 of slab i + 1, B(i + NUB) into
-    // its B unit in k-steps 1 and 2 of slab i + 1.  At the barrier of slab i a
-    // wave needs its loads of slab i + 1 landed; only the LB loads of
-    // B(i + NUB - 1) come after them.
+    // Loads: A(i) lives in A unit i mod 3, B(i) in B unit i mod 4; the
+    // barrier of slab i frees both units of slab i.  A(i + 2) goes into the A
+    // unit A(i - 1) left (first half after the barrier of slab i - 1, second
+    // half in k-step 0 of slab i), B(i + 3) into the B unit B(i - 1) left
+    // (k-steps 1 and 2 of slab i).  So both operands get about two slabs to
+    // land: the L2-resident A, which a decode-shaped call re-reads for every
+    // tile at twice B's bytes, as well as the streamed B.  In issue order, the
+    // loads after the last one of A(i + 1) when the barrier of slab i is
+    // reached are B(i + 2), A(i + 2) and B(i + 3): a wave has its loads of
+    // slab i + 1 landed once at most LA + 2 LB loads are in flight.
     auto main_loop = [&](auto nt) {
-        // Prologue: A(0), B(0) .. B(NUB - 2) and the first half of A(1); then
-        // slab 0 landed.
-#pragma unroll
-        for (int j = 0; j < LA; ++j)
-            issue_one(0, 0, 0, j, nt);
-#pragma unroll
-        for (int b = 0; b < NUB - 1; ++b)
-#pragma unroll
-            for (int j = 0; j < LB; ++j)
-                issue_one(1, b, b, j, nt);
+        // Prologue, in the order the loop would have issued it: A(0) first
+        // half, B(0), A(0) second half, B(1), A(1), B(2), A(2) first half;
+        // then slab 0 landed.
 #pragma unroll
         for (int j = 0; j < LA / 2; ++j)
+            issue_one(0, 0, 0, j, nt);
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            issue_one(1, 0, 0, j, nt);
+#pragma unroll
+        for (int j = LA / 2; j < LA; ++j)
+            issue_one(0, 0, 0, j, nt);
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            issue_one(1, 1, 1, j, nt);
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
             issue_one(0, 1, 1, j, nt);
-        wait_vmcnt<(NUB - 2) * LB + LA / 2>();
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            issue_one(1, 2, 2, j, nt);
+#pragma unroll
+        for (int j = 0; j < LA / 2; ++j)
+            issue_one(0, 2, 2, j, nt);
+        wait_vmcnt<2 * LB + 3 * LA / 2>();
         wg_barrier();
 #pragma unroll
         for (int n = 0; n < NR; ++n)
@@ -331,26 +349,26 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
 
         int ua = 0, ub = 0;                                 // units of slab i
         for (int i = 0; i < nk; ++i) {
-            const int ua1 = ua ^ 1;                         // A(i + 1), A(i - 1)
+            const int ua1 = ua == NUA - 1 ? 0 : ua + 1;     // A(i + 1)
+            const int ua2 = ua1 == NUA - 1 ? 0 : ua1 + 1;   // A(i + 2) = A(i - 1)
             const int ub1 = ub == NUB - 1 ? 0 : ub + 1;     // B(i + 1)
-            const int ubp = ub == 0 ? NUB - 1 : ub - 1;     // B(i - 1) = B(i + NUB - 1)
-            // k-step 0: the second half of A(i + 1)
-            kstep(0, ua, ub, 1, 1, [&](int k) { issue_one(0, i + 1, ua1, LA / 2 + k, nt); }, LA / 2, 0, MF);
-            // k-steps 1, 2: B(i + NUB - 1) into the unit B(i - 1) has left
+            const int ubp = ub == 0 ? NUB - 1 : ub - 1;     // B(i + 3) = B(i - 1)
+            // k-step 0: the second half of A(i + 2)
+            kstep(0, ua, ub, 1, 1, [&](int k) { issue_one(0, i + 2, ua2, LA / 2 + k, nt); }, LA / 2, 0, MF);
+            // k-steps 1, 2: B(i + 3)
             kstep(1, ua, ub, 2, 0, [&](int k) { issue_one(1, i + NUB - 1, ubp, k, nt); }, LB / 2, 0, MF);
             auto load_b2 = [&](int k) { issue_one(1, i + NUB - 1, ubp, LB / 2 + k, nt); };
             kstep(0, ua, ub, 3, 1, load_b2, LB / 2, 0, MF - 2);
             // every wave holds this slab's last fragments and has its own loads
-            // of slab i + 1 landed (B(i + NUB - 1) may be in flight); the
-            // barrier publishes both
+            // of slab i + 1 landed; the barrier publishes both
             wait_lgkmcnt0();
-            wait_vmcnt<LB>();
+            wait_vmcnt<LA + 2 * LB>();
             wg_barrier();
             __builtin_amdgcn_sched_barrier(0);
             kstep(0, ua, ub, 3, 1, load_b2, LB / 2, MF - 2, MF);
             // k-step 3: the first fragments of slab i + 1, and the first half of
-            // A(i + 2) into the unit A(i) has left
-            kstep(1, ua1, ub1, 0, 0, [&](int k) { issue_one(0, i + 2, ua, k, nt); }, LA / 2, 0, MF);
+            // A(i + 3) into the unit A(i) has left
+            kstep(1, ua1, ub1, 0, 0, [&](int k) { issue_one(0, i + 3, ua, k, nt); }, LA / 2, 0, MF);
             ua = ua1;
             ub = ub1;
         }

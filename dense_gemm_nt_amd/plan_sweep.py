@@ -7,7 +7,7 @@ taken in turn, so a clock or temperature drift hits every alternative alike).
 
 An alternative is a forced configuration, a forced K split count, or one of the
 handle's switches (GEMM_STREAMK, GEMM_INREDUCE), set while its handle is
-created.  Prints one JSON line per (shape, alternative) with the median, p10
+created.  Inputs rotate over enough sets to read cold, as in bench.py.  Prints one JSON line per (shape, alternative) with the median, p10
 and p90 over all rounds, marks the planner's own choice, and writes a Markdown
 table per sweep to --out.
 """
@@ -99,10 +99,21 @@ def _handle(g, env):
                 os.environ[k] = v
 
 
-def run_shape(g, shape, alts, rounds, per=20, sets=3):
+def input_sets(M, N, K, ind, outd):
+    """Rotating input sets for one shape: enough that together they exceed
+    600 MB, more than the 256 MB memory-side cache, so every launch reads its
+    operands cold, as bench.py's timings do (2 to 16 sets)."""
+    b = {"bf16": 2, "fp16": 2, "fp32": 4}
+    per = b[ind] * (M * K + N * K) + b[outd] * M * N
+    return max(2, min(16, -(-(600 << 20) // per)))
+
+
+def run_shape(g, shape, alts, rounds, per=20, sets=None):
     import torch
     from gemm_inputs import make_operands
     M, N, K, ind, outd, dist = shape
+    if sets is None:
+        sets = input_sets(M, N, K, ind, outd)
     dev = torch.device("cuda", 0)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
     bufs = []
@@ -158,8 +169,9 @@ def main():
           "Command: `python -m dense_gemm_nt_amd.plan_sweep --sweeps %s --rounds %d`" % (
               args.sweeps, args.rounds), "",
           "Median / p10 / p90 in us over %d interleaved rounds of 20 event-timed launches "
-          "per alternative (three rotating input sets).  `plan` is the library's own "
-          "choice, named in brackets." % args.rounds, ""]
+          "per alternative, on rotating input sets that together exceed 600 MB (cold "
+          "operands, as in bench.py).  `plan` is the library's own choice, named in "
+          "brackets." % args.rounds, ""]
     for name in args.sweeps.split(","):
         what, shapes, alts = SWEEPS[name]
         md += ["## %s" % name, "", what + ".", "",

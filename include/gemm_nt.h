@@ -73,8 +73,8 @@ typedef enum {
  * K splits off (every split plan then takes the second pass).
  * *out is NULL on error.  For measurement, GEMM_CONFIG=<name> forces one kernel
  * configuration, GEMM_SPLITS=<n> a K split on every call of this handle, and
- * GEMM_STREAMK=0/1/2 turns stream-K off (default), leaves it to the plan's
- * rule or uses it whenever the 256 x 256 ping-pong tile is planned; a GEMM_CONFIG that
+ * GEMM_STREAMK=0/1/2 turns stream-K off, leaves it to the plan (default) or
+ * uses it whenever the 256 x 256 ping-pong tile is planned; a GEMM_CONFIG that
  * names no configuration makes gemm_create return GEMM_ERR_INVALID_ARG.
  * GEMM_PERSIST=1 runs planned 256 x 256 ping-pong grids of more than 256
  * blocks with 256 persistent blocks.  GEMM_LOG=1 prints each call's plan to
@@ -96,15 +96,18 @@ gemm_status_t gemm_run(gemm_handle_t h, const void *A, const void *B, void *C,
 
 /* gemm_run for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  No handle:
- * split-K partials go to a static scratch array of
+ * split-K and stream-K partials go to a static scratch array of
  * GEMM_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which the library's code
  * object holds on each device it runs on from the first call there until the
  * process ends.  The call itself allocates nothing (no hipMalloc, hipFree or
  * allocating library routine).
- *   Arguments, results and errors as gemm_run on the current device with a
- *   handle made without GEMM_* switches: the same plan (its partials never
- *   need more than the scratch), so the same bits.  A plan that needed more
- *   scratch would return GEMM_ERR_UNSUPPORTED with nothing enqueued.
+ *   Arguments, results and errors as gemm_run on the current device (with a
+ *   handle made without GEMM_* switches), with one difference in the plan: a
+ *   stream-K plan whose partials would exceed the scratch takes the split plan
+ *   instead, so its results may differ from gemm_run's in the summation order
+ *   (within the same bound); every other plan is gemm_run's, with the same
+ *   bits.  A plan that still needed more scratch would return
+ *   GEMM_ERR_UNSUPPORTED with nothing enqueued.
  *   Every call on one device shares that device's scratch: two calls that may
  *   run concurrently on one device (different streams, or different host
  *   threads without ordering) race on it.  Serialise them, e.g. on one stream.

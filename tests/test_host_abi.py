@@ -137,10 +137,12 @@ def test_plan_regimes(g):
     # decode with few tiles splits K to cover the compute units
     p = g.gemm_plan(256, 8192, 8192)
     assert (p["splits"] > 1 or p["streamk"]) and p["workgroups"] >= 128
-    # few big tiles with a long K: the ping-pong tiles alone (stream-K is opt-in)
+    # few big tiles with a long K: stream-K over all 256 compute units; with a
+    # short K (runs under 32 k-slabs) or a well-filled split plan, not
     p = g.gemm_plan(3000, 3000, 5000)
-    assert p["streamk"] == 0 and p["workgroups"] == 144 and p["splits"] == 1
-    assert p["name"] == "256x256x64_w8_pp2"
+    assert p["streamk"] == 1 and p["workgroups"] == 256 and p["splits"] == 1
+    assert g.gemm_plan(3000, 3000, 1536)["streamk"] == 0
+    assert g.gemm_plan(2304, 2304, 8192)["streamk"] == 0
     assert g.gemm_plan(3000, 3000, 3000)["streamk"] == 0
     assert g.gemm_plan(256, 28672, 8192)["streamk"] == 0
     assert g.gemm_plan(4096, 4096, 4096)["streamk"] == 0
@@ -167,15 +169,18 @@ def test_plan_regimes(g):
     p = g.gemm_plan(256, 28672, 8192)
     assert p["splits"] == 2 and p["inreduce"] == 1
     assert p["workspace_bytes"] == p["tiles"] * 2 * p["block_m"] * p["block_n"] * 4
-    p = g.gemm_plan(256, 8192, 28672)
-    assert p["name"] == "256x256x64_w8_pp2" and p["splits"] > 2 and p["inreduce"] == 0
-    assert p["workspace_bytes"] == p["splits"] * 256 * 8192 * 4
-    # decode shapes the ping-pong tile would split more than four ways with a
-    # moderate K: the 256x128 tile with half the splits
-    for N in (10240, 8192):
-        p = g.gemm_plan(256, N, 8192)
+    # decode shapes the ping-pong tile would split more than four ways: the
+    # 256x128 tile with half the splits, more than two of them reduced by a
+    # second pass
+    for N, K in ((10240, 8192), (8192, 8192), (8192, 28672)):
+        p = g.gemm_plan(256, N, K)
         assert p["name"] == "256x128x64_w4_u8" and p["splits"] in (3, 4), p
+        assert p["inreduce"] == 0 and p["workspace_bytes"] == p["splits"] * 256 * N * 4
     assert g.gemm_plan(256, 28672, 8192)["name"] == "256x256x64_w8_pp2"
+    # more than two splits on the ping-pong tile take the second pass
+    p = g.gemm_plan(512, 8192, 8192)
+    assert p["name"] == "256x256x64_w8_pp2" and p["splits"] == 4 and p["inreduce"] == 0
+    assert p["workspace_bytes"] == 4 * 512 * 8192 * 4
     assert g.gemm_plan(4096, 4096, 4096)["inreduce"] == 0
     # the 4 KB stride rule only moves a split count the fill rule chose: with
     # at least 256 tiles there is one split, and it stays one

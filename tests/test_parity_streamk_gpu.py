@@ -93,23 +93,28 @@ def test_streamk_fused_epilogue(alpha, beta, along, act):
     check_epilogue(D, Dr, aS, t, "bf16", "stream-K epilogue")
 
 
-def test_streamk_rule_is_opt_in(capfd):
-    # the default plan never takes stream-K; GEMM_STREAMK=1 applies the rule,
-    # which picks it for (3000, 3000, 5000): 144 tiles, runs of ~44 k-slabs
+def test_streamk_is_planned_for_few_tiles_with_long_k(capfd):
+    # (3000, 3000, 5000): 144 tiles, runs of ~44 k-slabs; the default plan runs
+    # it as stream-K (the log line of the call says so), GEMM_STREAMK=0 as the
+    # plain plan, and both agree with the oracle
     M, N, K = 3000, 3000, 5000
     p = gemm_plan(M, N, K, _lib.GEMM_FP16, _lib.GEMM_FP32)
-    assert p["streamk"] == 0
-    say("case stream-K by the plan rule M=%d N=%d K=%d fp16->fp32" % (M, N, K))
-    os.environ["GEMM_LOG"] = "1"
-    try:
-        h = new_handle(streamk=1)
-    finally:
-        os.environ.pop("GEMM_LOG", None)
+    assert p["streamk"] == 1 and p["workgroups"] == 256
     A, B = make_operands(M, N, K, "fp16", "uniform", seed=5)
-    capfd.readouterr()
-    C = run_gpu(h, A, B, K, "fp16", "fp32")
-    err = capfd.readouterr().err
-    h.close()
-    assert "stream-K" in err and "grid=256" in err, err
     Cr, S = oracle.gemm_nt(A, B, K=K, in_dtype="fp16")
-    check(C, Cr, S, "fp32", "stream-K by the plan rule")
+    for streamk, tag in ((None, "stream-K"), (0, "")):
+        say("case stream-K rule M=%d N=%d K=%d fp16->fp32 GEMM_STREAMK=%s" % (M, N, K, streamk))
+        os.environ["GEMM_LOG"] = "1"
+        try:
+            h = new_handle(streamk=streamk)
+        finally:
+            os.environ.pop("GEMM_LOG", None)
+        capfd.readouterr()
+        C = run_gpu(h, A, B, K, "fp16", "fp32")
+        err = capfd.readouterr().err
+        h.close()
+        if tag:
+            assert tag in err and "grid=256" in err, err
+        else:
+            assert "stream-K" not in err and "grid=144" in err, err
+        check(C, Cr, S, "fp32", "GEMM_STREAMK=%s" % streamk)
