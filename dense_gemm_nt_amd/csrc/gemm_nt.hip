@@ -90,20 +90,20 @@ struct Config {
 // 32x32 MFMA tiles.  Configurations with kmask = 1 zero the operand columns past
 // K in registers and are the only ones planned when K is not a multiple of 8.
 const Config kConfigs[] = {
-    {"128x128x64_w4_s4", 128, 128, 64, 4, 4, 131072, 0, 1, gnt::kTile128x128_w4_s4},
-    {"128x128x64_w4_s4_kmask", 128, 128, 64, 4, 4, 131072, 1, 1, gnt::kTile128x128_w4_s4_kmask},
+    {"128x128x64_w8_s4", 128, 128, 64, 8, 4, 131072, 0, 1, gnt::kTile128x128_w8_s4},
+    {"128x128x64_w8_s4_kmask", 128, 128, 64, 8, 4, 131072, 1, 1, gnt::kTile128x128_w8_s4_kmask},
     {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk},
-    {"128x128x64_w4_s2", 128, 128, 64, 4, 2, 65536, 0, 1, gnt::kTile128x128_w4_s2},
+    {"128x128x64_w8_s2", 128, 128, 64, 8, 2, 65536, 0, 1, gnt::kTile128x128_w8_s2},
     {"32x128x64_w4_s6", 32, 128, 64, 4, 6, 122880, 0, 1, gnt::kTile32x128_w4_s6},
     {"256x128x64_w4_u8", 256, 128, 64, 4, 8, 163840, 0, 1, gnt::kW4_128},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
-    CFG_W4_128x128 = 0,
-    CFG_W4_128x128_KMASK = 1,
+    CFG_T128x128 = 0,
+    CFG_T128x128_KMASK = 1,
     CFG_PP2_256x256 = 2,
-    CFG_W4_128x128_S2 = 3,
-    CFG_W4_32x128 = 4,
+    CFG_T128x128_S2 = 3,
+    CFG_T32x128 = 4,
     CFG_W4_256x128 = 5,
 };
 
@@ -142,14 +142,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     if (force_cfg >= 0) {
         cfg = force_cfg;
     } else if (K % 8) {
-        cfg = CFG_W4_128x128_KMASK;
+        cfg = CFG_T128x128_KMASK;
     } else if (M <= 64) {
         // (at M = 64, two 32-row tiles per column still beat one 128-row tile:
         // 39.2 -> 36.8 us at 64x8192x8192, 19.9 -> 15.3 at 64x4096x4096; from
         // M = 96 the 128x128 tile is faster by half)
-        cfg = CFG_W4_32x128;
+        cfg = CFG_T32x128;
     } else if (M <= 128) {
-        cfg = CFG_W4_128x128;
+        cfg = CFG_T128x128;
     } else if (M <= 256) {
         // Decode batches: the whole of M in one 256-row tile of the ping-pong
         // kernel (A stays in L2, every compute unit streams its own 256-row
@@ -171,30 +171,30 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         // least 20 k-slabs each); smaller tiles otherwise.
         const int64_t big = std::max<int64_t>(1, cdiv(M, 256) * cdiv(N, 256));
         const int64_t ksplit = std::min<int64_t>(kNumCUs / big, cdiv(K, 64) / 20);
-        cfg = big * std::max<int64_t>(1, ksplit) >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_W4_128x128;
+        cfg = big * std::max<int64_t>(1, ksplit) >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_T128x128;
         // Small squares: the 32x128 tile, when without K splits it fills at
         // least as many compute units (in one pass) as the 128x128 tile does with
         // the splits the rule below gives it; it then needs no partials.
-        if (cfg == CFG_W4_128x128) {
+        if (cfg == CFG_T128x128) {
             const int64_t t128 = cdiv(M, 128) * cdiv(N, 128), t32 = cdiv(M, 32) * cdiv(N, 128);
             const int64_t kt = cdiv(K, 64);
             int64_t s128 = 1;
             if (t128 < kNumCUs && kt >= 16)
                 s128 = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / t128, kt / 8));
             if (t32 <= kNumCUs && t32 >= t128 * s128)
-                cfg = CFG_W4_32x128;
+                cfg = CFG_T32x128;
         }
     }
     // 128x128 tiles that overflow one pass of the machine but fit two: the
     // two-stage ring (64 KB of LDS) lets two blocks share a compute unit, so
     // they all run at once instead of leaving a second, nearly empty wave.
-    if (cfg == CFG_W4_128x128 && force_cfg < 0) {
+    if (cfg == CFG_T128x128 && force_cfg < 0) {
         const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
         if (t128 > kNumCUs && t128 <= 2 * kNumCUs)
-            cfg = CFG_W4_128x128_S2;
+            cfg = CFG_T128x128_S2;
     }
     if ((K % 8) && !kConfigs[cfg].kmask)
-        cfg = CFG_W4_128x128_KMASK;
+        cfg = CFG_T128x128_KMASK;
     const Config &c = kConfigs[cfg];
     p.cfg = cfg;
     p.tiles_m = (int)cdiv(M, c.bm);
@@ -224,7 +224,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     // together), so the nearest split count with another stride is taken.
     // Only when the fill rule split K: with one split no two blocks start in
     // the same B row.
-    if (cfg == CFG_W4_32x128 && M <= 32 && force_splits <= 0 && p.k_tiles >= 16 && splits > 1) {
+    if (cfg == CFG_T32x128 && M <= 32 && force_splits <= 0 && p.k_tiles >= 16 && splits > 1) {
         auto aliased = [&](int sp) { return (cdiv(p.k_tiles, sp) * c.bk * 2) % 4096 == 0; };
         auto ok = [&](int sp) { return sp >= 1 && sp <= 8 && p.k_tiles / sp >= 8 && !aliased(sp); };
         if (aliased(splits)) {

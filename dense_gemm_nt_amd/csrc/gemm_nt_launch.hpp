@@ -15,7 +15,7 @@ typedef hipError_t (*launch_fn)(const KernelArgs &, unsigned grid, hipStream_t);
 typedef launch_fn LaunchTable[2][3];
 
 // kernel-template tiles (gemm_nt_kernel.hpp), in the order of their names
-extern LaunchTable kTile128x128_w4_s4, kTile128x128_w4_s4_kmask, kTile128x128_w4_s2,
+extern LaunchTable kTile128x128_w8_s4, kTile128x128_w8_s4_kmask, kTile128x128_w8_s2,
     kTile32x128_w4_s6;
 // the 256x256 ping-pong kernel (gemm_nt_pp2.hpp), by operand layout: K-major A and B (NT), MN-major B, MN-major A,
 // both MN-major

@@ -21,10 +21,10 @@ static hipError_t launch_tile(const KernelArgs &a, unsigned grid, hipStream_t s)
     }
 
 #ifndef GNT_TILES_PART_B
-LaunchTable kTile128x128_w4_s4 = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, false);
+LaunchTable kTile128x128_w8_s4 = GNT_TILE_TABLE(128, 128, 64, 2, 4, 4, false);
 #else
-LaunchTable kTile128x128_w4_s4_kmask = GNT_TILE_TABLE(128, 128, 64, 2, 2, 4, true);
-LaunchTable kTile128x128_w4_s2 = GNT_TILE_TABLE(128, 128, 64, 2, 2, 2, false);
+LaunchTable kTile128x128_w8_s4_kmask = GNT_TILE_TABLE(128, 128, 64, 2, 4, 4, true);
+LaunchTable kTile128x128_w8_s2 = GNT_TILE_TABLE(128, 128, 64, 2, 4, 2, false);
 LaunchTable kTile32x128_w4_s6 = GNT_TILE_TABLE(32, 128, 64, 1, 4, 6, false);
 #endif
 

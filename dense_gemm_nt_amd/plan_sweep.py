@@ -24,7 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PP2, W4_256x128 = "256x256x64_w8_pp2", "256x128x64_w4_u8"
-T128, T128_S2, T32 = "128x128x64_w4_s4", "128x128x64_w4_s2", "32x128x64_w4_s6"
+T128, T128_S2, T32 = "128x128x64_w8_s4", "128x128x64_w8_s2", "32x128x64_w4_s6"
 
 # name: (what the rule decides, shapes (M, N, K, in, out, value distribution),
 #        alternatives (label, environment))

@@ -151,19 +151,19 @@ def test_plan_regimes(g):
     assert p["name"] == "256x256x64_w8_pp2" and p["splits"] > 1 and p["workgroups"] >= 128
     # ... and with a short K the smaller tile keeps the compute units busy: two
     # blocks per compute unit when its tiles overflow one pass of the machine
-    assert g.gemm_plan(1000, 4097, 1536)["name"] == "128x128x64_w4_s2"
-    assert g.gemm_plan(1000, 4096, 1536)["name"] == "128x128x64_w4_s4"
+    assert g.gemm_plan(1000, 4097, 1536)["name"] == "128x128x64_w8_s2"
+    assert g.gemm_plan(1000, 4096, 1536)["name"] == "128x128x64_w8_s4"
     # small squares: four times the blocks of the 32x128 tile, unless the
     # 128x128 tile with K splits fills as many compute units
     assert g.gemm_plan(512, 512, 512)["name"] == "32x128x64_w4_s6"
     assert g.gemm_plan(1024, 1024, 1024)["name"] == "32x128x64_w4_s6"
-    assert g.gemm_plan(640, 768, 8192)["name"] == "128x128x64_w4_s4"
+    assert g.gemm_plan(640, 768, 8192)["name"] == "128x128x64_w8_s4"
     # small M: the 32x128 tile up to M = 64, with split counts whose K starts
     # are not a multiple of 4 KB apart (for M <= 32); the 128x128 tile from M = 96
     p = g.gemm_plan(1, 8192, 8192)
     assert p["name"] == "32x128x64_w4_s6" and p["splits"] == 3
     assert g.gemm_plan(64, 8192, 8192)["name"] == "32x128x64_w4_s6"
-    assert g.gemm_plan(96, 28672, 8192)["name"] == "128x128x64_w4_s4"
+    assert g.gemm_plan(96, 28672, 8192)["name"] == "128x128x64_w8_s4"
     # two K splits on the 256-row tiles are reduced inside the kernel (one
     # 256 x 256 FP32 slot per split and tile); more splits take the second pass
     p = g.gemm_plan(256, 28672, 8192)

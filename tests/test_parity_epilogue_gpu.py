@@ -68,7 +68,7 @@ EPIS = [
 ]
 
 
-@pytest.mark.parametrize("config,splits", [("256x256x64_w8_pp2", None), ("128x128x64_w4_s4", None),
+@pytest.mark.parametrize("config,splits", [("256x256x64_w8_pp2", None), ("128x128x64_w8_s4", None),
                                            ("256x256x64_w8_pp2", 3), ("32x128x64_w4_s6", None)])
 @pytest.mark.parametrize("alpha,beta,along,act", EPIS)
 @pytest.mark.parametrize("out_dt", ["bf16", "fp32"])
@@ -95,7 +95,7 @@ def test_epilogue_small_integers_bitwise():
     g = torch.Generator().manual_seed(3)
     C_old = torch.randint(-50, 50, (M, N), generator=g).to(torch.float32)
     bias = torch.randint(-20, 20, (N,), generator=g).to(torch.float32)
-    for config in ("256x256x64_w8_pp2", "128x128x64_w4_s4"):
+    for config in ("256x256x64_w8_pp2", "128x128x64_w8_s4"):
         h = new_handle(config)
         D = _run_ex(h, A, B, K, "bf16", "fp32", C_old, 2.0, 1.0, bias, "n", "relu")
         h.close()

@@ -208,7 +208,7 @@ def test_fp8_argument_checks():
     assert st(sb=sc.data_ptr() + 2) == _lib.GEMM_ERR_INVALID_ARG  # misaligned scales
     assert _lib.gemm_run_fp8(h._h, 3, 3, p, p, C.data_ptr(), 16, 16, 32, 32, 32, 64, 0, None,
                              None, s) == _lib.GEMM_ERR_INVALID_ARG
-    h2 = new_handle("128x128x64_w4_s4")
+    h2 = new_handle("128x128x64_w8_s4")
     assert st(hh=h2) == _lib.GEMM_ERR_UNSUPPORTED                 # only the pp2 tile
     torch.cuda.synchronize()
     h2.close()

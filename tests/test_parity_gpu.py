@@ -17,8 +17,8 @@ from tests.gpu_util import compare_full, compare_sampled, new_handle, run_gpu, s
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = ["128x128x64_w4_s4", "128x128x64_w4_s4_kmask", "256x256x64_w8_pp2",
-           "128x128x64_w4_s2", "32x128x64_w4_s6", "256x128x64_w4_u8"]
+CONFIGS = ["128x128x64_w8_s4", "128x128x64_w8_s4_kmask", "256x256x64_w8_pp2",
+           "128x128x64_w8_s2", "32x128x64_w4_s6", "256x128x64_w4_u8"]
 
 
 @pytest.fixture(scope="module")
@@ -94,7 +94,7 @@ def test_small_integers_bitwise(config, splits):
     hh.close()
 
 
-@pytest.mark.parametrize("config", ["256x256x64_w8_pp2", "128x128x64_w4_s4", "256x128x64_w4_u8"])
+@pytest.mark.parametrize("config", ["256x256x64_w8_pp2", "128x128x64_w8_s4", "256x128x64_w4_u8"])
 @pytest.mark.parametrize("K", [8, 64, 128, 192, 200])
 def test_short_k_bitwise(config, K):
     # one to four k-slabs: the prologue and drain paths of the multi-slab rings

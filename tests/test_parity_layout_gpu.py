@@ -217,7 +217,7 @@ def test_layout_argument_checks():
     assert st(2, 0, 16, 16, 16, 16, 16) == _lib.GEMM_ERR_INVALID_ARG    # no such layout
     assert st(0, 0, 16, 16, 12, 16, 16) == _lib.GEMM_OK                 # NT takes any K
     assert st(1, 1, 16, 16, 16, 16, 16) == _lib.GEMM_OK
-    h2 = new_handle("128x128x64_w4_s4")
+    h2 = new_handle("128x128x64_w8_s4")
     assert st(1, 1, 16, 16, 16, 16, 16, hh=h2) == _lib.GEMM_ERR_UNSUPPORTED  # only the pp2 tile
     torch.cuda.synchronize()
     h2.close()

@@ -62,7 +62,7 @@ def test_default_plan_every_element(i):
 
 def test_the_draw_reaches_each_tile_family():
     names = {gemm_plan(M, N, K)["name"] for M, N, K in SHAPES}
-    assert {"32x128x64_w4_s6", "128x128x64_w4_s4", "128x128x64_w4_s2", "256x256x64_w8_pp2"} <= names, names
+    assert {"32x128x64_w4_s6", "128x128x64_w8_s4", "128x128x64_w8_s2", "256x256x64_w8_pp2"} <= names, names
 
 
 def test_plan_cache_over_many_shapes():
