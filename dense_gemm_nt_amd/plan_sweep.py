@@ -1,7 +1,8 @@
 """Timings behind the planner's rules: each named sweep runs the shapes a rule
 decides between, under every alternative the rule weighs, interleaved in one
 process (one library handle per alternative; rounds of event-timed launches
-taken in turn, so a clock or temperature drift hits every alternative alike).
+taken in turn, each round starting with another alternative, so that a clock
+or temperature drift and the order within a round favour none of them).
 
     python -m dense_gemm_nt_amd.plan_sweep [--sweeps a,b] [--rounds 8] [--out FILE.md]
 
@@ -138,8 +139,11 @@ def run_shape(g, shape, alts, rounds, per=20, sets=None):
                 for _ in range(5):
                     launch(h)
             torch.cuda.synchronize()
-        for _ in range(rounds):
-            for vi, h in enumerate(hs):
+        for r in range(rounds):
+            # each round starts with another alternative, so that a position in
+            # the round (what ran just before) favours none of them
+            for vi in [(r + k) % len(hs) for k in range(len(hs))]:
+                h = hs[vi]
                 for _ in range(5):
                     launch(h)
                 ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
