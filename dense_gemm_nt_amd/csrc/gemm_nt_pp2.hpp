@@ -104,6 +104,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
     KernelArgs p = p0;
 
     constexpr bool streamk = PS == 2;
+    // Grouped launches re-read row 0 for A loads wholly past M (see the loader):
+    // most of their tiles are partial.  A plain launch has at most one row of
+    // partial tiles, which waits for all loads instead, as with blockwise FP8
+    // scales, which have no register to spare for the redirect.
+    constexpr bool redirect_a = GR && SC != 1;
 
     // One output tile (split `split` of tile (tm, tn)): prologue, main loop and
     // epilogue.  Run once per block, or in a loop by persistent blocks.  A
@@ -141,6 +146,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         const int lc = (lane % CH) ^ row_key<CH>(lrow0);
         const uint32_t lda2 = (uint32_t)p.lda * ESZ, ldb2 = (uint32_t)p.ldb * ESZ;   // row pitch, bytes
         const uint32_t voffA = (uint32_t)lrow0 * lda2 + (uint32_t)lc * 16u;
+        const uint32_t voff0 = (uint32_t)lc * 16u;      // the same chunk of the tile's row 0
         const uint32_t voffB = (uint32_t)lrow0 * ldb2 + (uint32_t)lc * 16u;
         const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
@@ -180,15 +186,24 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                 const uint32_t v = (uint32_t)(4 * q + (lane >> 4)) * ld2 + (uint32_t)col * 2u;
                 load_lds16_policy<NT>(rs, v, (uint32_t)(16 * j) * ld2, dst);
             } else {
-                // rows past the tile's valid rows read zeros (see a_exact below
-                // for the waits that count on them)
+                // Rows past the tile's valid rows read zeros.  In a grouped
+                // launch, an A load all of whose eight rows lie past M re-reads
+                // the tile's row 0 instead (its LDS rows feed outputs that are
+                // never stored): a load out of range in every lane touches no
+                // memory and may count as done ahead of the loads issued before
+                // it, and group 1's waits count on the order of its A loads.
+                // (Its lane with logical chunk 0 is inside K: kt is below
+                // k_tiles.)  B's waits are all for every load, so B keeps the
+                // zero reads.
                 const uint32_t koff = (uint32_t)kt * (uint32_t)(BK * ESZ);
                 const bool kin = lc * 16 < (p.K - kt * BK) * ESZ;
                 const int row = row0 + 32 * j;
                 const int rows = IS_A ? rows_a : rows_b;
                 const uint32_t ld2 = IS_A ? lda2 : ldb2;
-                const uint32_t v = (kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange;
-                load_lds16_policy<NT>(IS_A ? rsA : rsB, v, koff + (uint32_t)row * ld2, dst);
+                const bool some = !IS_A || !redirect_a || row + 8 * q < rows;   // wave-uniform
+                const uint32_t v = some ? ((kin && lrow0 + row < rows) ? (IS_A ? voffA : voffB) : kOutOfRange)
+                                        : (kin ? voff0 : kOutOfRange);
+                load_lds16_policy<NT>(IS_A ? rsA : rsB, v, some ? koff + (uint32_t)row * ld2 : koff, dst);
             }
         };
         // The eight loads a wave issues in one memory phase, n = 0..7: group 0
@@ -408,12 +423,12 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // Group 1 waits with the loads of a later A slab in flight.  A load out
         // of range in every lane touches no memory and may count as done ahead
         // of the loads issued before it, which would let such a wait pass
-        // early; K-major A rows past M are such loads, and so are the k-rows
-        // past K of an MN-major A's last slab.  So the count-based waits are
-        // used only when no A load of the tile is wholly out of range: a
-        // K-major A with all 256 rows inside M (MN-major columns past M are
-        // clamped instead), and never with the MN-major last slab in flight.
-        const bool a_exact = AM || rows_a == BM;
+        // early.  No MN-major A load is (columns past M are clamped), nor a
+        // K-major one with the row-0 redirect; without it the count-based waits
+        // need every A row inside M.  The k-rows past K of an MN-major A's last
+        // slab are such loads too: the count-based waits are never used with
+        // that slab in flight.
+        const bool a_exact = AM || redirect_a || rows_a == BM;
         if (nk > 0) {
             // Prologue: B(0) by group 0; A(0), A(1) by group 1.  Slab 0 lands before
             // phase 0; A(1) by the end of phase 1 (the steady-state wait).
