@@ -19,7 +19,7 @@ SOURCES = [os.path.join(CSRC, f) for f in (
     "launch_pp2_f8_e4e4.hip", "launch_pp2_f8_e4e5.hip", "launch_pp2_f8_e5e4.hip",
     "launch_pp2_f8_e5e5.hip", "launch_pp2_grouped.hip", "launch_pp2_persistent.hip", "launch_w4.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gemm_nt_common.hpp", "gemm_nt_kernel.hpp",
-                                           "gemm_nt_pp2.hpp", "gemm_nt_w4.hpp",
+                                           "gemm_nt_pp2.hpp", "gemm_nt_w4.hpp", "gemm_nt_trace.hpp",
                                            "gemm_nt_launch.hpp", "launch_pp2.hip",
                                            "launch_pp2_f8.hip", "launch_tiles_a.hip")] + \
     [os.path.join(ROOT, "include", "gemm_nt.h")]
@@ -56,26 +56,28 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
+def build(verbose: bool = False, jobs: int = 0, out: str = LIB, defines=()) -> str:
+    """Compile every source and link them into `out` (the library by default;
+    `defines` are extra -D flags, e.g. for an instrumented copy)."""
     tmpdir = tempfile.mkdtemp(prefix="gemm_nt_build_")
     try:
         objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
-        cmds = [[hipcc(), *flags(), "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        cmds = [[hipcc(), *flags(), *defines, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
         jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 8))
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
         with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
             list(ex.map(_run, cmds))
-        tmp = LIB + ".tmp%d" % os.getpid()
+        tmp = out + ".tmp%d" % os.getpid()
         link = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
         if verbose:
             print(" ".join(link), flush=True)
         _run(link)
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return LIB
+    return out
 
 
 def stale() -> bool:

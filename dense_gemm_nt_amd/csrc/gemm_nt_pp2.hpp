@@ -7,8 +7,8 @@
 // workgroup barrier ends every phase.  Both groups load.  Issuing the 64
 // wave-wide 1 KB loads of a slab takes longer than one compute phase when a
 // single group issues all of them: the vector memory unit accepts a wave-wide 16-byte-per-
-// lane load every ~25 cycles, so the loading waves stall on issue, not on
-// latency.  Here each group issues half a slab in its own memory phase, while
+// lane load every 25-40 cycles (more when it misses L2), so the loading waves
+// stall on issue, not on latency.  Here each group issues half a slab in its own memory phase, while
 // the other group keeps the matrix cores busy ("A Blackwell GEMM by Hand in
 // CuTe DSL", section 3: the producer's copies overlap the consumer's MMAs;
 // section 7: enough stages in flight for the load latency).
@@ -60,8 +60,15 @@
 
 #include "gemm_nt_common.hpp"
 
-#ifndef GNT_PP2_EVENT
-#define GNT_PP2_EVENT(i, e)   // instrumentation hook (phase events); empty in the library
+#ifdef GNT_PP2_TRACE
+#include "gemm_nt_trace.hpp"
+#else
+// instrumentation hooks (phase timestamps, gemm_nt_trace.hpp); empty in the library
+#define GNT_PP2_TRACE_LDS 0
+#define GNT_PP2_TRACE_DECL
+#define GNT_PP2_EVENT(i, e)
+#define GNT_PP2_FLUSH(g, i)
+#define GNT_PP2_DUMP
 #endif
 
 namespace gnt {
@@ -88,7 +95,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
     // blockwise scales: A_0 rows in two 512-byte slots, A_1 rows in three, B's
     // two column blocks in two 256-byte slots
     constexpr int SA0 = UNITS * UNIT, SA1 = SA0 + 2 * 512, SB = SA1 + 3 * 512;
-    constexpr int LDS_BYTES = UNITS * UNIT + (SC ? 2 * 512 + 3 * 512 + 2 * 256 : 0);
+    constexpr int LDS_USED = UNITS * UNIT + (SC ? 2 * 512 + 3 * 512 + 2 * 256 : 0);
+    constexpr int LDS_BYTES = LDS_USED + GNT_PP2_TRACE_LDS;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
@@ -429,6 +437,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // slab are such loads too: the count-based waits are never used with
         // that slab in flight.
         const bool a_exact = AM || redirect_a || rows_a == BM;
+        GNT_PP2_TRACE_DECL
         if (nk > 0) {
             // Prologue: B(0) by group 0; A(0), A(1) by group 1.  Slab 0 lands before
             // phase 0; A(1) by the end of phase 1 (the steady-state wait).
@@ -455,6 +464,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                         GNT_PP2_EVENT(i, 0);
                         memory_phase(G0{}, i, i + 1 < nk, i + 1, nt);    // B(i+1)
                         wait_lgkmcnt0();
+                        GNT_PP2_FLUSH(0, i);
                         GNT_PP2_EVENT(i, 1);
                         phase_end();                               // end of phase 2i
                         GNT_PP2_EVENT(i, 2);
@@ -483,6 +493,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
                     GNT_PP2_EVENT(i, 2);
                     memory_phase(G1{}, i, i + 2 < nk, i + 2, std::false_type{}, g1_rows);   // A(i+2)
                     wait_lgkmcnt0();
+                    GNT_PP2_FLUSH(1, i);
                     GNT_PP2_EVENT(i, 3);
                     if (a_exact && (i + 3 < nk || (i + 2 < nk && !AM)))   // A(i+1) landed
                         wait_vmcnt<A_INFLIGHT>();
@@ -496,6 +507,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             }
         }
 
+        GNT_PP2_DUMP
         // Epilogue (the ring is free: the last fragment read and the last load
         // completed before the loop's last barrier).  Each wave stages its own
         // 64 x 128 block in its own 16 KB of LDS.
