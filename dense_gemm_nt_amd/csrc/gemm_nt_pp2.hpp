@@ -6,9 +6,10 @@
 // loads) and a compute phase (the 32 MFMAs of one 64-deep k-slab), and a
 // workgroup barrier ends every phase.  Both groups load.  Issuing the 64
 // wave-wide 1 KB loads of a slab takes longer than one compute phase when a
-// single group issues all of them: the vector memory unit accepts a wave-wide 16-byte-per-
-// lane load every 25-40 cycles (more when it misses L2), so the loading waves
-// stall on issue, not on latency.  Here each group issues half a slab in its own memory phase, while
+// single group issues all of them: with the LDS also serving the other
+// group's fragment reads, a wave-wide 16-byte-per-lane load costs its wave
+// 25-40 cycles of issue (its LDS write queues behind the reads), so the
+// loading waves stall on issue, not on latency.  Here each group issues half a slab in its own memory phase, while
 // the other group keeps the matrix cores busy ("A Blackwell GEMM by Hand in
 // CuTe DSL", section 3: the producer's copies overlap the consumer's MMAs;
 // section 7: enough stages in flight for the load latency).
