@@ -1,4 +1,4 @@
-"""Host models of the LDS ring schedules of two kernels (no GPU).
+"""Host models of the LDS ring schedules of three kernels (no GPU).
 
 Each model lists, in program order, what one wave issues: direct-to-LDS loads
 (operand, slab, ring unit), `vmcnt` waits, workgroup barriers and fragment
@@ -14,6 +14,9 @@ completed when it arrived.  The checks, for every slab count up to 40:
 - slabs past the split's end are loaded only into units no real slab reads
   afterwards (the kernels re-read the last slab there to keep wait counts
   uniform).
+The ping-pong kernel's two wave groups run different programs; its model
+(at the end) checks the same two properties across the groups, a load being
+published by the barrier after the issuing group's wait that covers it.
 """
 import pytest
 
@@ -195,3 +198,131 @@ def test_tile_ring_model_catches_a_short_wait():
     bad.ev = [("wait", 2 * 8 + 1) if e == ("wait", 2 * 8) else e for e in w.ev]
     with pytest.raises(AssertionError):
         check(bad, 10)
+
+
+# ---------------------------------------------------------------------------
+# The ping-pong kernel (gemm_nt_pp2.hpp): two groups of waves, each with its own
+# program; a workgroup barrier ends every phase, so the programs are cut into
+# the same number of segments.  Group 0 loads B and reads A_0 and B; group 1
+# loads A (both halves) and reads A_1 and B.  A wave's waits count its own
+# loads only; a load is published at the barrier ending the segment of the
+# wait that completed it.  Units: B slot s = units ("B", 2 s), ("B", 2 s + 1);
+# A_0 slot s = ("A0", s), s < 2; A_1 slot s = ("A1", s), s < 3.
+
+PP_LOADS = 8          # wave-wide loads per wave and slab (4 per half)
+
+
+def pp2_programs(nk, am=False, a_exact=True, g1_wait=PP_LOADS, b_slots=2, a1_slots=3):
+    """Per group, a list of segments; a segment is a list of events
+    ("load", key, slab), ("wait", n), ("read", key, slab)."""
+    g0, g1 = [[]], [[]]
+
+    def b_load(seg, i):
+        for half in (0, 1):
+            for _ in range(PP_LOADS // 2):
+                seg.append(("load", ("B", 2 * (i % b_slots) + half), i))
+
+    def a_load(seg, i):
+        for _ in range(PP_LOADS // 2):
+            seg.append(("load", ("A0", i % 2), i))
+        for _ in range(PP_LOADS // 2):
+            seg.append(("load", ("A1", i % a1_slots), i))
+
+    # prologue: B(0) by group 0; A(0), A(1) by group 1
+    b_load(g0[-1], 0)
+    g0[-1].append(("wait", 0))
+    a_load(g1[-1], 0)
+    if nk > 1:
+        a_load(g1[-1], 1)
+    g1[-1].append(("wait", g1_wait if a_exact and (nk > 2 or (nk == 2 and not am)) else 0))
+    for i in range(nk):
+        # phase 2i: group 0 loads B(i+1), reads A_0(i) and B(i); group 1 computes
+        g0.append([])
+        if i + 1 < nk:
+            b_load(g0[-1], i + 1)
+        g0[-1] += [("read", ("A0", i % 2), i), ("read", ("B", 2 * (i % b_slots)), i),
+                   ("read", ("B", 2 * (i % b_slots) + 1), i)]
+        g1.append([])
+        # phase 2i+1: group 0 computes, then waits for B(i+1); group 1 loads
+        # A(i+2), reads A_1(i) and B(i), waits for A(i+1)
+        g0.append([("wait", 0)])
+        g1.append([])
+        if i + 2 < nk:
+            a_load(g1[-1], i + 2)
+        g1[-1] += [("read", ("A1", i % a1_slots), i), ("read", ("B", 2 * (i % b_slots)), i),
+                   ("read", ("B", 2 * (i % b_slots) + 1), i)]
+        exact = a_exact and (i + 3 < nk or (i + 2 < nk and not am))
+        g1[-1].append(("wait", g1_wait if exact else 0))
+    return g0, g1
+
+
+def pp2_check(groups, nk):
+    nseg = len(groups[0])
+    assert all(len(g) == nseg for g in groups)
+    # completion segment of every load, per group (a wait completes all but the
+    # last n loads that group issued)
+    published = {}          # (key, slab) -> list of segments at whose end each load is published
+    for g in groups:
+        issued = []         # (key, slab, segment issued)
+        done = 0
+        for k, seg in enumerate(g):
+            for e in seg:
+                if e[0] == "load":
+                    issued.append((e[1], e[2]))
+                elif e[0] == "wait":
+                    upto = max(done, len(issued) - e[1])
+                    for key, slab in issued[done:upto]:
+                        published.setdefault((key, slab), []).append(k)
+                    done = upto
+        assert done == len(issued), "loads left in flight at the end"
+    # what each unit holds, in segment order (loads of a segment land before
+    # its reads by another group only if published earlier: checked below)
+    last_read = {}          # (key, slab) -> latest segment it is read in
+    loads_at = {}           # key -> list of (segment, slab)
+    for gi, g in enumerate(groups):
+        for k, seg in enumerate(g):
+            for e in seg:
+                if e[0] == "load":
+                    loads_at.setdefault(e[1], []).append((k, e[2]))
+                elif e[0] == "read":
+                    last_read[(e[1], e[2])] = max(last_read.get((e[1], e[2]), -1), k)
+    for gi, g in enumerate(groups):
+        for k, seg in enumerate(g):
+            for e in seg:
+                if e[0] != "read":
+                    continue
+                key, slab = e[1], e[2]
+                assert slab < nk
+                # every load of this slab into this unit published before segment k
+                segs = published.get((key, slab))
+                assert segs, ("read of a slab never loaded", e)
+                assert len(segs) == PP_LOADS // 2 and max(segs) <= k - 1, ("read before publication", gi, k, e, segs)
+                # the unit still holds this slab: no later slab loaded into it
+                # in a segment up to k
+                later = [s for s, sl in loads_at[key] if sl != slab and sl > slab and s <= k]
+                assert not later, ("unit overwritten before the read", gi, k, e)
+    # WAR: a load into a unit only after every read of its previous slab
+    for key, lst in loads_at.items():
+        for k, slab in lst:
+            prev = [sl for s, sl in lst if sl < slab]
+            if prev:
+                p = max(prev)
+                assert last_read.get((key, p), -1) <= k - 1, ("load over a unit still read", key, slab, k)
+
+
+@pytest.mark.parametrize("am", [False, True])
+def test_ping_pong_ring(am):
+    for nk in range(1, 41):
+        pp2_check(pp2_programs(nk, am=am), nk)
+
+
+def test_ping_pong_ring_model_catches_mistakes():
+    # one load fewer allowed in flight passes; one more reads A before it lands
+    pp2_check(pp2_programs(12, g1_wait=PP_LOADS - 1), 12)
+    with pytest.raises(AssertionError):
+        pp2_check(pp2_programs(12, g1_wait=PP_LOADS + 1), 12)
+    # B with one slot, or A_1 with two, overwrites a unit that is still read
+    with pytest.raises(AssertionError):
+        pp2_check(pp2_programs(12, b_slots=1), 12)
+    with pytest.raises(AssertionError):
+        pp2_check(pp2_programs(12, a1_slots=2), 12)
