@@ -53,6 +53,13 @@ SWEEPS = {
          (1500, 2900, 1024, "bf16", "bf16", "uniform")],
         [("plan", {}), (T128, {"GEMM_CONFIG": T128}), (T128_S2, {"GEMM_CONFIG": T128_S2}),
          (PP2, {"GEMM_CONFIG": PP2})]),
+    "small_m_fill": (
+        "M <= 32: K splits for about three quarters of the compute units (rounded), "
+        "not all of them",
+        [(1, 4096, 16384, "bf16", "bf16", "llm"), (1, 2048, 32768, "bf16", "bf16", "llm"),
+         (16, 4096, 4096, "bf16", "bf16", "llm"), (1, 4096, 8192, "bf16", "bf16", "llm")],
+        [("plan", {})] + [("%s splits=%d" % (T32, s), {"GEMM_CONFIG": T32, "GEMM_SPLITS": str(s)})
+                          for s in (4, 5, 8, 16)]),
     "split_stride": (
         "M <= 32 with K splits: split counts whose starts are a multiple of 4 KB "
         "apart are moved to the nearest count that is not",
@@ -66,6 +73,22 @@ SWEEPS = {
         [(3000, 3000, 5000, "fp16", "fp32", "uniform"), (2304, 2304, 8192, "bf16", "bf16", "uniform"),
          (3000, 3000, 1536, "fp16", "fp32", "uniform")],
         [("plan", {}), ("stream-K off", {"GEMM_STREAMK": "0"}), ("stream-K on", {"GEMM_STREAMK": "2"})]),
+    "decode_splits": (
+        "few-tile decode shapes: the four-wave tile's three or four K splits with a second "
+        "pass, against two splits reduced in the kernel, and against one split",
+        [(256, 10240, 8192, "bf16", "bf16", "llm"), (256, 8192, 8192, "bf16", "bf16", "llm"),
+         (256, 8192, 28672, "bf16", "bf16", "llm")],
+        [("plan", {}), ("%s 2 splits" % W4_256x128, {"GEMM_CONFIG": W4_256x128, "GEMM_SPLITS": "2"}),
+         ("%s 1 split" % W4_256x128, {"GEMM_CONFIG": W4_256x128, "GEMM_SPLITS": "1"}),
+         ("%s 2 splits" % PP2, {"GEMM_CONFIG": PP2, "GEMM_SPLITS": "2"})]),
+    "mid_four_wave": (
+        "mid-size shapes: the planned tile against the four-wave 256x128 tile, whose "
+        "wave blocks read fewer LDS bytes per FLOP",
+        [(1000, 4097, 1536, "fp16", "fp32", "uniform"), (1024, 4096, 2048, "bf16", "bf16", "uniform"),
+         (1500, 2900, 1024, "bf16", "bf16", "uniform"), (1536, 1536, 1536, "bf16", "fp32", "uniform"),
+         (2048, 2048, 2048, "bf16", "fp32", "uniform"), (127, 28672, 8192, "fp16", "fp32", "uniform"),
+         (3000, 3000, 5000, "fp16", "fp32", "uniform")],
+        [("plan", {}), (W4_256x128, {"GEMM_CONFIG": W4_256x128})]),
     "in_kernel_reduction": (
         "two K splits on the 256-row tiles: the second split to finish adds the "
         "first's partial, instead of a second pass",

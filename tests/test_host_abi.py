@@ -162,7 +162,15 @@ def test_plan_regimes(g):
     # are not a multiple of 4 KB apart (for M <= 32); the 128x128 tile from M = 96
     p = g.gemm_plan(1, 8192, 8192)
     assert p["name"] == "32x128x64_w4_s6" and p["splits"] == 3
-    assert g.gemm_plan(64, 8192, 8192)["name"] == "32x128x64_w4_s6"
+    # for M <= 32 the K splits aim at about three quarters of the compute
+    # units (rounded), not all of them
+    for (M, N, K), sp in (((1, 4096, 16384), 6), ((1, 2048, 32768), 12), ((16, 4096, 4096), 6),
+                          ((1, 16384, 8192), 3), ((1, 6144, 8192), 3)):
+        p = g.gemm_plan(M, N, K)
+        assert p["name"] == "32x128x64_w4_s6" and p["splits"] == sp, (M, N, K, p)
+    # M = 64 (two tile rows sharing B) still fills every compute unit
+    p = g.gemm_plan(64, 8192, 8192)
+    assert p["name"] == "32x128x64_w4_s6" and p["splits"] == 2 and p["workgroups"] == 256
     assert g.gemm_plan(96, 28672, 8192)["name"] == "128x128x64_w8_s4"
     # two K splits on the 256-row tiles are reduced inside the kernel (one
     # 256 x 256 FP32 slot per split and tile); more splits take the second pass
