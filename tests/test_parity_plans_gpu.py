@@ -81,3 +81,20 @@ def test_plan_cache_over_many_shapes():
         h2.close()
         assert np.array_equal(C, R), (M, N, K)
     h.close()
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(1, 4096, 16384, 6), (1, 2048, 32768, 12), (16, 4096, 4096, 6),
+                                          (7, 6144, 8192, 3)])
+def test_small_m_split_counts_every_element(M, N, K, splits):
+    # M <= 32: the K splits aim at three quarters of the compute units; every
+    # element of those split counts against the oracle, partials summed by
+    # the second pass
+    p = gemm_plan(M, N, K, CODE["bf16"], CODE["bf16"])
+    assert p["name"] == "32x128x64_w4_s6" and p["splits"] == splits, p
+    say("case small-M plan M=%d N=%d K=%d splits=%d" % (M, N, K, splits))
+    h = new_handle()
+    A, B = make_operands(M, N, K, "bf16", "llm", seed=M + splits)
+    C = run_gpu(h, A, B, K, "bf16", "bf16")
+    err, worst = compare_full(C, A, B, K, "bf16", "bf16", "M=%d N=%d K=%d" % (M, N, K))
+    say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
+    h.close()
