@@ -253,6 +253,24 @@ def test_large_leading_dimension(h):
     compare_full(C, A, B, K, "bf16", "fp32", "lda=2^22-8")
 
 
+@pytest.mark.parametrize("config", ["256x256x64_w8_pp2", "256x128x64_w4_u8", "128x128x64_w8_s4"])
+@pytest.mark.parametrize("which", ["a", "b"])
+def test_largest_leading_dimension_on_the_big_tiles(config, which):
+    # lda (or ldb) just below the library's limit on the 256- and 128-row
+    # tiles, whose row offsets times the pitch come closest to the 32-bit
+    # range of a buffer load's offset and of a tile's buffer size; two tile
+    # rows (the second ragged) and a ragged column tile
+    M, N, K, ld = 260, 300, 128, (1 << 22) - 8
+    say("case ld%s = 2^22-8 on %s M=%d N=%d K=%d" % (which, config, M, N, K))
+    A, B = make_operands(M, N, K, "bf16", "uniform", seed=5, lda=ld if which == "a" else K,
+                         ldb=ld if which == "b" else K)
+    hc = new_handle(config)
+    C = run_gpu(hc, A, B, K, "bf16", "fp32")
+    hc.close()
+    compare_full(C, A, B, K, "bf16", "fp32", "%s ld%s=2^22-8" % (config, which))
+    del A, B
+
+
 def test_misaligned_operand_is_rejected_without_launch(h):
     say("case misaligned A")
     dev = torch.device("cuda", 0)
