@@ -98,3 +98,19 @@ def test_small_m_split_counts_every_element(M, N, K, splits):
     err, worst = compare_full(C, A, B, K, "bf16", "bf16", "M=%d N=%d K=%d" % (M, N, K))
     say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
     h.close()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 1 << 20), (5, 260, (1 << 18) + 8)])
+def test_longest_k_every_element(M, N, K):
+    # one or three tiles with a K of a million: the split rule's largest
+    # counts (191 and 64 splits of the 32-row tile), the ordered second pass
+    # over all of them, and a ragged last split
+    p = gemm_plan(M, N, K, CODE["bf16"], CODE["fp32"])
+    say("case longest K M=%d N=%d K=%d %s splits=%d" % (M, N, K, p["name"], p["splits"]))
+    assert p["splits"] >= 64, p
+    h = new_handle()
+    A, B = make_operands(M, N, K, "bf16", "uniform", seed=K % 97)
+    C = run_gpu(h, A, B, K, "bf16", "fp32")
+    err, worst = compare_full(C, A, B, K, "bf16", "fp32", "M=%d N=%d K=%d" % (M, N, K))
+    say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
+    h.close()
