@@ -271,6 +271,28 @@ def test_largest_leading_dimension_on_the_big_tiles(config, which):
     del A, B
 
 
+def test_output_beyond_two_to_the_31_elements(h):
+    # C with more than 2^31 elements (4.3 GB of BF16): the store offsets of its
+    # last rows exceed the 32-bit range; rows on both sides of the boundary
+    # against the oracle (C stays on the GPU: only those rows come back)
+    from tests.tolerance import check
+    M, N, K = 65600, 32768, 16
+    assert M * N > 2 ** 31
+    say("case output past 2^31 elements M=%d N=%d K=%d" % (M, N, K))
+    A, B = make_operands(M, N, K, "bf16", "uniform", seed=11)
+    dev = torch.device("cuda", 0)
+    Ad, Bd = A.to(dev), B.to(dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    h.run_raw(Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), M, N, K, K, K, N, 0, 0, 0)
+    torch.cuda.synchronize()
+    rows = [0, (2 ** 31) // N - 1, (2 ** 31) // N, M - 1]
+    got = C[rows].float().cpu().double().numpy()
+    Cr, S = oracle.gemm_nt_rows(A, B, rows, K=K, in_dtype="bf16")
+    check(got, Cr, S, "bf16", "rows around 2^31 elements")
+    del Ad, Bd, C
+    torch.cuda.empty_cache()
+
+
 def test_misaligned_operand_is_rejected_without_launch(h):
     say("case misaligned A")
     dev = torch.device("cuda", 0)
