@@ -73,10 +73,15 @@ def test_grouped_small_integers_bitwise():
         assert np.array_equal(C.cpu().double().numpy(), Cr), g
 
 
-def test_grouped_matches_one_launch_per_group_bitwise():
+@pytest.mark.parametrize("shapes", [
+    [(300, 280, 2048), (512, 512, 1024), (40, 300, 512)],
+    # a mixture-of-experts token mix, one tile row each: A loads wholly past a
+    # problem's rows re-read its row 0 in the grouped launch and read zeros in
+    # a plain one; the outputs they feed are never stored
+    [(m, 512, 1024) for m in (64, 17, 200, 3, 90, 128, 256, 40, 1, 129)]])
+def test_grouped_matches_one_launch_per_group_bitwise(shapes):
     # the same tile kernel without K splits: the same MFMA order, the same bits
-    shapes = [(300, 280, 2048), (512, 512, 1024), (40, 300, 512)]
-    say("case grouped vs per-group launches")
+    say("case grouped vs per-group launches, %d groups" % len(shapes))
     host, dev, probs, outs = _problems(shapes, "bf16", "uniform", 2, "bf16")
     h = new_handle()
     assert _launch(h, probs, "bf16", "bf16") == _lib.GEMM_OK
