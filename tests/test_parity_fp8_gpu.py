@@ -25,20 +25,21 @@ DEV = torch.device("cuda", 0)
 FMT = {"e4m3": _lib.GEMM_FP8_E4M3, "e5m2": _lib.GEMM_FP8_E5M2}
 
 
-def _run(h, A, B, sa, sb, K, fa, fb, mode, block_m, out_dt, epi=None, C_old=None):
+def _run(h, A, B, sa, sb, K, fa, fb, mode, block_m, out_dt, epi=None, C_old=None, ldc=None):
     M, lda = A.shape
     N, ldb = B.shape
+    ldc = N if ldc is None else ldc
     Ad, Bd, sad, sbd = A.to(DEV), B.to(DEV), sa.to(DEV), sb.to(DEV)
     if C_old is None:
-        Cd = torch.full((max(M, 1), max(N, 1)), float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
+        Cd = torch.full((max(M, 1), max(ldc, 1)), float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
     else:
         Cd = C_old.to(DEV).clone()
     scales = _lib.fp8_scales(mode, sad.data_ptr(), sbd.data_ptr(), block_m)
     s = torch.cuda.current_stream(DEV)
     h.run_raw_fp8(FMT[fa], FMT[fb], Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), M, N, K, lda, ldb,
-                  N, CODE[out_dt], scales, epi, s.cuda_stream)
+                  ldc, CODE[out_dt], scales, epi, s.cuda_stream)
     s.synchronize()
-    return Cd[:M, :N].float().cpu().to(torch.float64).numpy()
+    return Cd[:M, :ldc].float().cpu().to(torch.float64).numpy()
 
 
 def _oracle(A, B, sa, sb, K, fa, fb, mode, block_m):
@@ -80,6 +81,23 @@ def test_fp8_small_integers_bitwise(mode, block_m, splits):
     h.close()
     Cr, _ = _oracle(A, B, sa, sb, K, "e4m3", "e5m2", mode, block_m)
     assert np.array_equal(C, Cr)
+
+
+@pytest.mark.parametrize("mode,block_m", [("tensor", 1), ("block", 128)])
+@pytest.mark.parametrize("out_dt,pad", [("fp32", 1), ("bf16", 3)])
+def test_fp8_unaligned_ldc(mode, block_m, out_dt, pad):
+    # rows of C not a multiple of 16 bytes apart: the stores take the
+    # unaligned path; a whole 256 tile and ragged edges, padding left alone
+    M, N, K = 300, 280, 256
+    say("case fp8 ldc=N+%d %s %s/%d" % (pad, out_dt, mode, block_m))
+    A, B, sa, sb = make_fp8_operands(M, N, K, "e4m3", "e4m3", "uniform", seed=9, mode=mode,
+                                     block_m=block_m)
+    h = new_handle()
+    C = _run(h, A, B, sa, sb, K, "e4m3", "e4m3", mode, block_m, out_dt, ldc=N + pad)
+    h.close()
+    assert np.isnan(C[:, N:]).all()
+    Cr, S = _oracle(A, B, sa, sb, K, "e4m3", "e4m3", mode, block_m)
+    check(C[:, :N], Cr, S, out_dt, "fp8 ldc=N+%d" % pad)
 
 
 @pytest.mark.parametrize("K", [16, 128, 144])
