@@ -27,19 +27,21 @@ LAYOUT = {"k": _lib.GEMM_K_MAJOR, "mn": _lib.GEMM_MN_MAJOR}
 OTHER = [("k", "mn"), ("mn", "k"), ("mn", "mn")]
 
 
-def _run(h, la, lb, Xa, Xb, M, N, K, in_dt, out_dt, epi=None, C_old=None):
-    """C on the GPU from stored arrays; C_old (host, out_dt) is C's prior content."""
+def _run(h, la, lb, Xa, Xb, M, N, K, in_dt, out_dt, epi=None, C_old=None, ldc=None):
+    """C on the GPU from stored arrays; C_old (host, out_dt) is C's prior content.
+    Returns the stored rows of C, ldc (default N) columns wide."""
     lda, ldb = Xa.shape[1], Xb.shape[1]
+    ldc = N if ldc is None else ldc
     Ad, Bd = Xa.to(DEV), Xb.to(DEV)
     if C_old is None:
-        Cd = torch.full((max(M, 1), max(N, 1)), float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
+        Cd = torch.full((max(M, 1), max(ldc, 1)), float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
     else:
         Cd = C_old.to(DEV).clone()
     s = torch.cuda.current_stream(DEV)
     h.run_raw_layout(LAYOUT[la], LAYOUT[lb], Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), M, N, K,
-                     lda, ldb, N, CODE[in_dt], CODE[out_dt], epi, s.cuda_stream)
+                     lda, ldb, ldc, CODE[in_dt], CODE[out_dt], epi, s.cuda_stream)
     s.synchronize()
-    return Cd[:M, :N].float().cpu().to(torch.float64).numpy()
+    return Cd[:M, :ldc].float().cpu().to(torch.float64).numpy()
 
 
 def _views(Xa, Xb, la, lb, M, N, K):
@@ -74,6 +76,23 @@ def test_layout_every_element(la, lb, in_dt, out_dt):
     Cr, S = oracle.gemm(Va, Vb, la, lb, in_dtype=in_dt)
     err, worst = check(C, Cr, S, out_dt, "layout %s%s" % (la, lb))
     say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
+
+
+@pytest.mark.parametrize("la,lb", OTHER)
+@pytest.mark.parametrize("out_dt,pad", [("fp32", 1), ("bf16", 3)])
+def test_layout_unaligned_ldc(la, lb, out_dt, pad):
+    # rows of C not a multiple of 16 bytes apart on the MN-major kernels: the
+    # unaligned store path, padding columns left alone
+    M, N, K = 300, 280, 200
+    say("case layout %s%s ldc=N+%d out=%s" % (la, lb, pad, out_dt))
+    Xa, Xb = _stored(M, N, K, la, lb, "bf16", "uniform", seed=4)
+    h = new_handle()
+    C = _run(h, la, lb, Xa, Xb, M, N, K, "bf16", out_dt, ldc=N + pad)
+    h.close()
+    assert np.isnan(C[:, N:]).all()
+    Va, Vb = _views(Xa, Xb, la, lb, M, N, K)
+    Cr, S = oracle.gemm(Va, Vb, la, lb, in_dtype="bf16")
+    check(C[:, :N], Cr, S, out_dt, "layout %s%s ldc=N+%d" % (la, lb, pad))
 
 
 @pytest.mark.parametrize("la,lb", OTHER)
