@@ -63,6 +63,32 @@ def test_grouped_every_element(dt, out_dt):
         check(C.float().cpu().double().numpy(), Cr, S, out_dt, "group %d %r" % (g, SHAPES[g]))
 
 
+@pytest.mark.parametrize("out_dt", ["fp32", "bf16"])
+def test_grouped_unaligned_ldc(out_dt):
+    # each group's C rows a different, unaligned number of elements apart;
+    # the padding columns stay untouched
+    shapes = [(300, 280, 200), (64, 700, 512), (3, 129, 72)]
+    pads = [1, 3, 5]
+    say("case grouped ldc=N+pad %s" % out_dt)
+    host, dev, outs = [], [], []
+    for g, ((M, N, K), pad) in enumerate(zip(shapes, pads)):
+        A, B = make_operands(M, N, K, "bf16", "uniform", seed=30 + g)
+        host.append((A, B, K))
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        Cd = torch.full((M, N + pad), float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
+        dev.append((Ad, Bd, Cd))
+    probs = [_lib.GemmGroupProblem(Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), None, M, N, K, K, K,
+                                   N + pad)
+             for (Ad, Bd, Cd), (M, N, K), pad in zip(dev, shapes, pads)]
+    h = new_handle()
+    assert _launch(h, probs, "bf16", out_dt) == _lib.GEMM_OK
+    h.close()
+    for g, ((Cr, S), (_, _, Cd), (M, N, K)) in enumerate(zip(oracle.gemm_grouped(host), dev, shapes)):
+        C = Cd.float().cpu().double().numpy()
+        assert np.isnan(C[:, N:]).all(), g
+        check(C[:, :N], Cr, S, out_dt, "group %d ldc=N+%d" % (g, pads[g]))
+
+
 def test_grouped_small_integers_bitwise():
     say("case grouped int3 bitwise")
     host, dev, probs, outs = _problems(SHAPES, "bf16", "int3", 5, "fp32")
