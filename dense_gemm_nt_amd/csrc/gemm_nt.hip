@@ -124,6 +124,16 @@ struct Plan {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Whether tiles start their k-slabs at rotated slabs (KernelArgs::slab_rot;
+// `mode` as GEMM_ROTATE).  A function of the problem, not of the plan, so that
+// every tile family gives an output the same summation order.  Rotation
+// spreads the blocks' row offsets over the memory channels, which pays where
+// B streams from HBM and A is small (M <= 128: 1 x 4096 x 16384 38.0 -> 28.3
+// us, 127 x 28672 x 8192 102.6 -> 95.4); with 256 rows of A every tile reads,
+// tiles at different slabs no longer share A's slabs in L2 as they go
+// (256 x 8192 x 8192: 57.3 -> 62.3 us), and from there on it measured level.
+bool rotate_slabs(int mode, int64_t M) { return mode == 2 || (mode == 1 && M <= 128); }
+
 int find_config(const char *name)
 {
     for (int i = 0; i < kNumConfigs; ++i)
@@ -331,6 +341,8 @@ struct gemm_handle_s {
     int inreduce;      // GEMM_INREDUCE: 1 (default) two K splits reduced in the kernel, 0 never
     int streamk;       // GEMM_STREAMK: 0 off, 1 by the plan rule (default), 2 whenever
                        // the ping-pong tile is planned
+    int rotate;        // GEMM_ROTATE: rotated k-slab starts per 256-column block (KernelArgs::slab_rot):
+                       // 0 never, 1 by the rule of rotate_slabs (default), 2 always
     int log;
     // grouped launches: pinned staging of the problem list and an event that
     // marks when the last copy out of it has run
@@ -478,6 +490,9 @@ gemm_status_t gemm_create(gemm_handle_t *out)
         h->streamk = atoi(e);
     if (const char *e = getenv("GEMM_LOG"))
         h->log = atoi(e);
+    h->rotate = 1;
+    if (const char *e = getenv("GEMM_ROTATE"))
+        h->rotate = atoi(e);
     h->ws_bytes = mb << 20;
     h->inreduce = 1;
     if (const char *e = getenv("GEMM_INREDUCE"))
@@ -576,12 +591,14 @@ struct Workspace {
     int64_t bytes;         // for partials and grouped problem lists
     unsigned *counters;    // GEMM_COUNTER_BYTES of arrival counters
     int log;
+    int rotate;            // KernelArgs::slab_rot
 };
 
 Workspace workspace_of(gemm_handle_t h)
 {
     return Workspace{h->partials, h->ws_bytes,
-                     reinterpret_cast<unsigned *>(reinterpret_cast<uint8_t *>(h->partials) + h->ws_bytes), h->log};
+                     reinterpret_cast<unsigned *>(reinterpret_cast<uint8_t *>(h->partials) + h->ws_bytes), h->log,
+                     h->rotate};
 }
 
 // Fill the plan-, output- and epilogue-dependent fields of `a` (whose operand
@@ -617,6 +634,7 @@ gemm_status_t enqueue(const Workspace &ws, const Plan &p, KernelArgs &a, launch_
     a.sk_maxseg = p.sk_maxseg;
     a.inreduce = p.inreduce;
     a.counters = ws.counters;
+    a.slab_rot = rotate_slabs(ws.rotate, M);
     a.alpha = 1.0f;
     if (epi) {
         a.alpha = epi->alpha;
@@ -750,7 +768,7 @@ gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C, int64_t M,
     launch_fn fn = p.stream ? gnt::kPP2_streamk[in_dtype][out_dtype]
                             : kConfigs[p.cfg].fn[in_dtype][out_dtype];
     const Workspace ws{static_cast<float *>(ptr), GEMM_NOALLOC_SCRATCH_BYTES,
-                       reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ptr) + GEMM_NOALLOC_SCRATCH_BYTES), 0};
+                       reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ptr) + GEMM_NOALLOC_SCRATCH_BYTES), 0, 1};
     return enqueue(ws, p, a, fn, C, M, N, K, ldc, out_dtype, nullptr, stream);
 }
 
@@ -871,7 +889,7 @@ gemm_status_t run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
         d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
                   (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
                   (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0) |
-                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0);
+                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0) | (rotate_slabs(h->rotate, q.M) ? gnt::GD_ROTATE : 0);
         descs.push_back(d);
         tiles += (int64_t)d.tiles_m * d.tiles_n;
         if (tiles >= INT32_MAX)
@@ -953,7 +971,7 @@ gemm_status_t run_grouped_fp8(gemm_handle_t h, int a_dtype, int b_dtype,
         d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
                   (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
                   (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0) |
-                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0);
+                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0) | (rotate_slabs(h->rotate, q.M) ? gnt::GD_ROTATE : 0);
         descs.push_back(d);
         tiles += (int64_t)d.tiles_m * d.tiles_n;
         if (tiles >= INT32_MAX)

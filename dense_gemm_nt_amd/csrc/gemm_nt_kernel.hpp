@@ -76,6 +76,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt_begin = split * p.kt_per_split;
     const int kt_end = min(p.k_tiles, kt_begin + p.kt_per_split);
+    const SlabOrder order = slab_order(kt_begin, kt_end - kt_begin, p.k_tiles, p.K % BK != 0, n0, p.slab_rot);
 
     const int rows_a = min(BM, p.M - m0);
     const int rows_b = min(BN, p.N - n0);
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
         // most the (STAGES - 2) NL loads of the slabs after it are in flight.
         // Issued at once, the loads past the end are skipped instead, and the
         // last iterations wait for everything.
-        auto slab_kt = [&](int i) { return kt_begin + min(i, nkt - 1); };
+        auto slab_kt = [&](int i) { return order(min(i, nkt - 1)); };
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (!EARLY || s < nkt)
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
 
             const uint8_t *sa = smem + s * A_BYTES + wave_m * WTM * PITCH;
             const uint8_t *sb = smem + STAGES * A_BYTES + s * B_BYTES + wave_n * WTN * PITCH;
-            const int kt = kt_begin + i;
+            const int kt = order(i);
             // When K is not a multiple of 8 the slab holding column K-1 also holds
             // columns past K in its last chunk (the row's padding); KMASK builds
             // zero those in registers.  Without it K % 8 == 0 is required.

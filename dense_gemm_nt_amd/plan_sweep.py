@@ -7,7 +7,7 @@ or temperature drift and the order within a round favour none of them).
     python -m dense_gemm_nt_amd.plan_sweep [--sweeps a,b] [--rounds 8] [--out FILE.md]
 
 An alternative is a forced configuration, a forced K split count, or one of the
-handle's switches (GEMM_STREAMK, GEMM_INREDUCE), set while its handle is
+handle's switches (GEMM_STREAMK, GEMM_INREDUCE, GEMM_ROTATE), set while its handle is
 created.  Inputs rotate over enough sets to read cold, as in bench.py.  Prints one JSON line per (shape, alternative) with the median, p10
 and p90 over all rounds, marks the planner's own choice, and writes a Markdown
 table per sweep to --out.
@@ -89,6 +89,17 @@ SWEEPS = {
          (2048, 2048, 2048, "bf16", "fp32", "uniform"), (127, 28672, 8192, "fp16", "fp32", "uniform"),
          (3000, 3000, 5000, "fp16", "fp32", "uniform")],
         [("plan", {}), (W4_256x128, {"GEMM_CONFIG": W4_256x128})]),
+    "slab_rotation": (
+        "each 256-column block of tiles starting its k-slabs at a rotated slab when M <= 128, "
+        "against every tile walking K from its first slab, and against rotation at every M",
+        [(256, 28672, 8192, "bf16", "bf16", "llm"), (256, 8192, 28672, "bf16", "bf16", "llm"),
+         (256, 10240, 8192, "bf16", "bf16", "llm"), (256, 8192, 8192, "bf16", "bf16", "llm"),
+         (1, 8192, 8192, "bf16", "bf16", "llm"), (32, 8192, 8192, "bf16", "bf16", "llm"),
+         (1, 4096, 16384, "bf16", "bf16", "llm"), (127, 28672, 8192, "fp16", "fp32", "uniform"),
+         (512, 8192, 8192, "bf16", "bf16", "llm"), (4096, 4096, 4096, "bf16", "bf16", "uniform"),
+         (8192, 8192, 8192, "bf16", "bf16", "uniform"), (8192, 28672, 8192, "bf16", "bf16", "llm"),
+         (1000, 4097, 1536, "fp16", "fp32", "uniform"), (2048, 2048, 2048, "bf16", "fp32", "uniform")],
+        [("plan", {}), ("natural order", {"GEMM_ROTATE": "0"}), ("rotated", {"GEMM_ROTATE": "2"})]),
     "in_kernel_reduction": (
         "two K splits on the 256-row tiles: the second split to finish adds the "
         "first's partial, instead of a second pass",
@@ -97,7 +108,8 @@ SWEEPS = {
 }
 
 CODE = {"bf16": 0, "fp16": 1, "fp32": 2}
-ENV_KEYS = ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_STREAMK", "GEMM_INREDUCE", "GEMM_PERSIST")
+ENV_KEYS = ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_STREAMK", "GEMM_INREDUCE", "GEMM_PERSIST",
+            "GEMM_ROTATE")
 
 
 def _pct(xs, q):

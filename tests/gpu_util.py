@@ -20,15 +20,20 @@ def say(msg):
     sys.stdout.flush()
 
 
-def new_handle(config=None, splits=None, persistent=False, streamk=None, inreduce=None):
+def new_handle(config=None, splits=None, persistent=False, streamk=None, inreduce=None, rotate=None):
     """A fresh library handle; `config` / `splits` force the plan for this handle,
     `persistent` runs its ping-pong tiles with persistent blocks, `streamk`
     (0 / 1 / 2) sets its stream-K mode (default: the plan rule), `inreduce`
-    (0 / 1) the in-kernel reduction of two K splits (default: on)."""
+    (0 / 1) the in-kernel reduction of two K splits (default: on), `rotate`
+    (0 / 1 / 2) the k-slab order (natural, the M <= 128 rule (default), rotated)."""
     from dense_gemm_nt_amd import Gemm
     old = {k: os.environ.get(k) for k in ("GEMM_CONFIG", "GEMM_SPLITS", "GEMM_PERSIST", "GEMM_STREAMK",
-                                          "GEMM_INREDUCE")}
+                                          "GEMM_INREDUCE", "GEMM_ROTATE")}
     try:
+        if rotate is not None:
+            os.environ["GEMM_ROTATE"] = str(rotate)
+        else:
+            os.environ.pop("GEMM_ROTATE", None)
         if inreduce is not None:
             os.environ["GEMM_INREDUCE"] = str(inreduce)
         else:

@@ -95,6 +95,32 @@ def test_layout_unaligned_ldc(la, lb, out_dt, pad):
     check(C[:, :N], Cr, S, out_dt, "layout %s%s ldc=N+%d" % (la, lb, pad))
 
 
+@pytest.mark.parametrize("la,lb", [("k", "k")] + OTHER)
+@pytest.mark.parametrize("splits", [None, 2])
+def test_layout_rotated_slab_order(la, lb, splits):
+    # k-slabs in the rotated order (GEMM_ROTATE=2) on every layout: K = 1000 is
+    # 15 slabs of 64 and a partial last one, which keeps its place; 600
+    # columns are three 256-column blocks, so three different starts.  Random
+    # values against the oracle, and small integers bitwise against the
+    # natural order (exact sums, so any order gives the same bits).
+    M, N, K = 100, 600, 1000
+    say("case layout rotated order %s%s splits=%s" % (la, lb, splits))
+    for dist in ("uniform", "int3"):
+        Xa, Xb = _stored(M, N, K, la, lb, "bf16", dist, seed=6, pad=8)
+        h2 = new_handle(None, splits, rotate=2)
+        C = _run(h2, la, lb, Xa, Xb, M, N, K, "bf16", "fp32")
+        h2.close()
+        Va, Vb = _views(Xa, Xb, la, lb, M, N, K)
+        Cr, S = oracle.gemm(Va, Vb, la, lb, in_dtype="bf16")
+        if dist == "uniform":
+            check(C, Cr, S, "fp32", "layout %s%s rotated" % (la, lb))
+        else:
+            h0 = new_handle(None, splits, rotate=0)
+            C0 = _run(h0, la, lb, Xa, Xb, M, N, K, "bf16", "fp32")
+            h0.close()
+            assert np.array_equal(C, Cr) and np.array_equal(C0, Cr)
+
+
 @pytest.mark.parametrize("la,lb", OTHER)
 @pytest.mark.parametrize("splits", [None, 3])
 def test_layout_small_integers_bitwise(la, lb, splits):
