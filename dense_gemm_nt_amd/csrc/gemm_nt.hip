@@ -83,6 +83,7 @@ struct Config {
     int kmask;      // zeroes operand columns past K in registers (any K)
     int splitk;     // supports splits > 1
     launch_fn (*fn)[3];   // [in dtype][out dtype]
+    launch_fn (*fn_rot)[3];   // the same tiles in the rotated k-slab order (or null)
 };
 
 // The kernel family.  The kernel-template tiles use stages * (BM + BN) * BK * 2
@@ -90,12 +91,13 @@ struct Config {
 // 32x32 MFMA tiles.  Configurations with kmask = 1 zero the operand columns past
 // K in registers and are the only ones planned when K is not a multiple of 8.
 const Config kConfigs[] = {
-    {"128x128x64_w8_s4", 128, 128, 64, 8, 4, 131072, 0, 1, gnt::kTile128x128_w8_s4},
-    {"128x128x64_w8_s4_kmask", 128, 128, 64, 8, 4, 131072, 1, 1, gnt::kTile128x128_w8_s4_kmask},
-    {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk},
-    {"128x128x64_w8_s2", 128, 128, 64, 8, 2, 65536, 0, 1, gnt::kTile128x128_w8_s2},
-    {"32x128x64_w4_s6", 32, 128, 64, 4, 6, 122880, 0, 1, gnt::kTile32x128_w4_s6},
-    {"256x128x64_w4_u8", 256, 128, 64, 4, 8, 163840, 0, 1, gnt::kW4_128},
+    {"128x128x64_w8_s4", 128, 128, 64, 8, 4, 131072, 0, 1, gnt::kTile128x128_w8_s4, gnt::kTile128x128_w8_s4_rot},
+    {"128x128x64_w8_s4_kmask", 128, 128, 64, 8, 4, 131072, 1, 1, gnt::kTile128x128_w8_s4_kmask,
+     gnt::kTile128x128_w8_s4_kmask_rot},
+    {"256x256x64_w8_pp2", 256, 256, 64, 8, 9, 147456, 0, 1, gnt::kPP2_kk, nullptr},
+    {"128x128x64_w8_s2", 128, 128, 64, 8, 2, 65536, 0, 1, gnt::kTile128x128_w8_s2, gnt::kTile128x128_w8_s2_rot},
+    {"32x128x64_w4_s6", 32, 128, 64, 4, 6, 122880, 0, 1, gnt::kTile32x128_w4_s6, gnt::kTile32x128_w4_s6_rot},
+    {"256x128x64_w4_u8", 256, 128, 64, 4, 8, 163840, 0, 1, gnt::kW4_128, nullptr},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum {
@@ -124,15 +126,24 @@ struct Plan {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Whether tiles start their k-slabs at rotated slabs (KernelArgs::slab_rot;
-// `mode` as GEMM_ROTATE).  A function of the problem, not of the plan, so that
-// every tile family gives an output the same summation order.  Rotation
-// spreads the blocks' row offsets over the memory channels, which pays where
-// B streams from HBM and A is small (M <= 128: 1 x 4096 x 16384 38.0 -> 28.3
-// us, 127 x 28672 x 8192 102.6 -> 95.4); with 256 rows of A every tile reads,
-// tiles at different slabs no longer share A's slabs in L2 as they go
-// (256 x 8192 x 8192: 57.3 -> 62.3 us), and from there on it measured level.
+// Whether the tile kernels (32x128, 128x128) walk their k-slabs in the
+// rotated order (SlabOrder; `mode` as GEMM_ROTATE).  Rotation spreads the
+// blocks' row offsets over the memory channels, which pays where B streams
+// from HBM and A is small (M <= 128: 1 x 4096 x 16384 38.0 -> 28.3 us,
+// 127 x 28672 x 8192 102.6 -> 95.4, 1 x 8192 x 8192 30.0 -> 28.2).  With 256
+// rows of A that every tile reads, tiles at different slabs no longer share
+// A's slabs in L2 as they go (256 x 8192 x 8192 on the four-wave tile: 57.3
+// -> 62.3 us), and on the large shapes it measured level or slower, so the
+// 256-row tiles always walk K in order.
 bool rotate_slabs(int mode, int64_t M) { return mode == 2 || (mode == 1 && M <= 128); }
+
+// The launch function of configuration `cfg`, in the rotated slab order when
+// `rot` and the configuration has one.
+launch_fn config_fn(int cfg, bool rot, int in_dtype, int out_dtype)
+{
+    const Config &c = kConfigs[cfg];
+    return (rot && c.fn_rot ? c.fn_rot : c.fn)[in_dtype][out_dtype];
+}
 
 int find_config(const char *name)
 {
@@ -341,8 +352,8 @@ struct gemm_handle_s {
     int inreduce;      // GEMM_INREDUCE: 1 (default) two K splits reduced in the kernel, 0 never
     int streamk;       // GEMM_STREAMK: 0 off, 1 by the plan rule (default), 2 whenever
                        // the ping-pong tile is planned
-    int rotate;        // GEMM_ROTATE: rotated k-slab starts per 256-column block (KernelArgs::slab_rot):
-                       // 0 never, 1 by the rule of rotate_slabs (default), 2 always
+    int rotate;        // GEMM_ROTATE: the tile kernels' rotated k-slab order (SlabOrder): 0 never,
+                       // 1 by the rule of rotate_slabs (default), 2 always
     int log;
     // grouped launches: pinned staging of the problem list and an event that
     // marks when the last copy out of it has run
@@ -591,14 +602,12 @@ struct Workspace {
     int64_t bytes;         // for partials and grouped problem lists
     unsigned *counters;    // GEMM_COUNTER_BYTES of arrival counters
     int log;
-    int rotate;            // KernelArgs::slab_rot
 };
 
 Workspace workspace_of(gemm_handle_t h)
 {
     return Workspace{h->partials, h->ws_bytes,
-                     reinterpret_cast<unsigned *>(reinterpret_cast<uint8_t *>(h->partials) + h->ws_bytes), h->log,
-                     h->rotate};
+                     reinterpret_cast<unsigned *>(reinterpret_cast<uint8_t *>(h->partials) + h->ws_bytes), h->log};
 }
 
 // Fill the plan-, output- and epilogue-dependent fields of `a` (whose operand
@@ -634,7 +643,6 @@ gemm_status_t enqueue(const Workspace &ws, const Plan &p, KernelArgs &a, launch_
     a.sk_maxseg = p.sk_maxseg;
     a.inreduce = p.inreduce;
     a.counters = ws.counters;
-    a.slab_rot = rotate_slabs(ws.rotate, M);
     a.alpha = 1.0f;
     if (epi) {
         a.alpha = epi->alpha;
@@ -697,7 +705,7 @@ gemm_status_t gemm_run_layout(gemm_handle_t h, int layout_a, int layout_b, const
     a.B = static_cast<const uint16_t *>(B);
     a.lda = (int)lda;
     a.ldb = (int)ldb;
-    launch_fn fn = nt ? kConfigs[p.cfg].fn[in_dtype][out_dtype]
+    launch_fn fn = nt ? config_fn(p.cfg, rotate_slabs(h->rotate, M), in_dtype, out_dtype)
                       : kLayoutFns[2 * am + bnm - 1][in_dtype][out_dtype];
     Plan q = p;
     if (p.stream) {
@@ -766,9 +774,9 @@ gemm_status_t gemm_run_noalloc(const void *A, const void *B, void *C, int64_t M,
     a.lda = (int)lda;
     a.ldb = (int)ldb;
     launch_fn fn = p.stream ? gnt::kPP2_streamk[in_dtype][out_dtype]
-                            : kConfigs[p.cfg].fn[in_dtype][out_dtype];
+                            : config_fn(p.cfg, rotate_slabs(1, M), in_dtype, out_dtype);
     const Workspace ws{static_cast<float *>(ptr), GEMM_NOALLOC_SCRATCH_BYTES,
-                       reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ptr) + GEMM_NOALLOC_SCRATCH_BYTES), 0, 1};
+                       reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ptr) + GEMM_NOALLOC_SCRATCH_BYTES), 0};
     return enqueue(ws, p, a, fn, C, M, N, K, ldc, out_dtype, nullptr, stream);
 }
 
@@ -889,7 +897,7 @@ gemm_status_t run_grouped(gemm_handle_t h, const gemm_group_problem_t *problems,
         d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
                   (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
                   (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0) |
-                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0) | (rotate_slabs(h->rotate, q.M) ? gnt::GD_ROTATE : 0);
+                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0);
         descs.push_back(d);
         tiles += (int64_t)d.tiles_m * d.tiles_n;
         if (tiles >= INT32_MAX)
@@ -971,7 +979,7 @@ gemm_status_t run_grouped_fp8(gemm_handle_t h, int a_dtype, int b_dtype,
         d.flags = ((q.ldc % 4 == 0) && ((uintptr_t)q.C % vec_bytes == 0) ? gnt::GD_VEC_STORE : 0) |
                   (((q.ldc * out_size) % 16 == 0) && ((uintptr_t)q.C % 16 == 0) ? gnt::GD_ROWS16 : 0) |
                   (d.bias && (uintptr_t)d.bias % 16 == 0 ? gnt::GD_BIAS_VEC : 0) |
-                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0) | (rotate_slabs(h->rotate, q.M) ? gnt::GD_ROTATE : 0);
+                  (d.tiles_m <= 2 ? gnt::GD_NT_B : 0);
         descs.push_back(d);
         tiles += (int64_t)d.tiles_m * d.tiles_n;
         if (tiles >= INT32_MAX)

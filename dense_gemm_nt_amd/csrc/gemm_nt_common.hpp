@@ -34,13 +34,13 @@ struct GroupDesc {
     int lda, ldb, ldc;     // elements
     int tile_start;        // the group's first position in the launch's tile list
     int tiles_m, tiles_n, k_tiles;
-    int flags;             // GD_VEC_STORE | GD_ROWS16 | GD_BIAS_VEC | GD_NT_B | GD_ROTATE
+    int flags;             // GD_VEC_STORE | GD_ROWS16 | GD_BIAS_VEC | GD_NT_B
     int sf_ld;             // FP8: k-blocks per scale row
     const float *scale_a;  // FP8: this group's scales (per tensor or blockwise)
     const float *scale_b;
     uint32_t sfa_bytes, sfb_bytes;
 };
-enum : int { GD_VEC_STORE = 1, GD_ROWS16 = 2, GD_BIAS_VEC = 4, GD_NT_B = 8, GD_ROTATE = 16 };
+enum : int { GD_VEC_STORE = 1, GD_ROWS16 = 2, GD_BIAS_VEC = 4, GD_NT_B = 8 };
 
 struct KernelArgs {
     const uint16_t *A;
@@ -84,43 +84,50 @@ struct KernelArgs {
     // grouped launch: the problems, and each launch position's problem index
     const GroupDesc *groups;
     const int *tile_group;
-    int slab_rot;          // 1: each tile starts its k-slabs at a rotated slab (SlabOrder)
 };
 
 // The order in which a tile visits the k-slabs of its range [kt0, kt0 + nk).
-// Local slab i is slab kt0 + (i + rot) mod nf for i < nf.  Here nf counts the
-// range's whole slabs, and rot = (n0 / 256) mod nf for a tile whose first
-// column is n0.  A partial last slab of K keeps its place at the end, where
-// the kernels' K-tail handling expects it.  So tiles of neighbouring
-// 256-column blocks start at different slabs.  When every block walks K in
-// step, all the rows a launch reads at one moment sit at one offset within
-// their row.  With a power-of-two row pitch those addresses share their low
-// bits, and the requests load a few memory channels only.  A streaming probe
-// of a decode-shaped B operand (28672 rows of 16 KB, 224 blocks reading 128
-// bytes of 256 rows per step) reached 4.7 TB/s in step and 6.1 TB/s with the
-// starts rotated.  The slab sum is the same sum in another order.  That order
-// depends only on an output's 256-column block and its split's range: every
-// launch of a shape gives the same bits, and so do tiles of other widths
-// over the same splits.
+// With ROT, local slab i is slab kt0 + (i + rot) mod nf for i < nf.  Here nf
+// counts the range's whole slabs, and rot = (n0 / 256) mod nf for a tile
+// whose first column is n0.  A partial last slab of K keeps its place at the
+// end, where the kernels' K-tail handling expects it.  So tiles of
+// neighbouring 256-column blocks start at different slabs.  When every block
+// walks K in step, all the rows a launch reads at one moment sit at one
+// offset within their row.  With a power-of-two row pitch those addresses
+// share their low bits, and the requests load a few memory channels only.  A
+// streaming probe of a decode-shaped B operand (28672 rows of 16 KB, 224
+// blocks reading 128 bytes of 256 rows per step) reached 4.7 TB/s in step and
+// 6.1 TB/s with the starts rotated.  The slab sum is the same sum in another
+// order, fixed by an output's 256-column block and its split's range: every
+// launch of a shape gives the same bits.  Without ROT, slab kt0 + i: the
+// order is a template parameter because its few scalar instructions per slab
+// measured about 1% on the large shapes, which never rotate.
+template <bool ROT>
 struct SlabOrder {
     int kt0, nf, rot;
     __device__ __forceinline__ int operator()(int i) const
     {
-        if (i >= nf)
+        if constexpr (!ROT)
             return kt0 + i;
         const int j = i + rot;
-        return kt0 + (j < nf ? j : j - nf);
+        const int r = j - (j >= nf ? nf : 0);
+        return kt0 + (i < nf ? r : i);
     }
 };
 
-// `partial_last`: K is not a multiple of the slab depth; `rotate` 0 keeps the
-// natural order (stream-K segments, GEMM_ROTATE=0).
-__device__ __forceinline__ SlabOrder slab_order(int kt0, int nk, int k_tiles, bool partial_last, int n0,
-                                                int rotate)
+// `partial_last`: K is not a multiple of the slab depth.
+template <bool ROT>
+__device__ __forceinline__ SlabOrder<ROT> slab_order(int kt0, int nk, int k_tiles, bool partial_last, int n0)
 {
+    if constexpr (!ROT)
+        return SlabOrder<ROT>{kt0, nk, 0};
     const int nf = nk - ((partial_last && kt0 + nk == k_tiles) ? 1 : 0);
-    return SlabOrder{kt0, nf, (rotate && nf > 1) ? (n0 >> 8) % nf : 0};
+    return SlabOrder<ROT>{kt0, nf, nf > 1 ? (n0 >> 8) % nf : 0};
 }
+
+// Keep a scalar computed where it stands: the empty asm reads and writes it,
+// so the arithmetic behind it cannot sink past the barriers to its first use.
+__device__ __forceinline__ void pin_scalar(int &x) { asm volatile("" : "+s"(x)); }
 
 // Byte offset added to a load that must return zeros: beyond every buffer's
 // num_records, so the buffer unit returns 0 without touching memory.

@@ -44,7 +44,8 @@
 
 namespace gnt {
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int IN, int OUT, bool KMASK>
+// ROT: the tiles walk their k-slabs in the rotated order (SlabOrder).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int IN, int OUT, bool KMASK, bool ROT>
 __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
 {
     constexpr int NWAVES = WM * WN;
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt_begin = split * p.kt_per_split;
     const int kt_end = min(p.k_tiles, kt_begin + p.kt_per_split);
-    const SlabOrder order = slab_order(kt_begin, kt_end - kt_begin, p.k_tiles, p.K % BK != 0, n0, p.slab_rot);
+    const SlabOrder<ROT> order = slab_order<ROT>(kt_begin, kt_end - kt_begin, p.k_tiles, p.K % BK != 0, n0);
 
     const int rows_a = min(BM, p.M - m0);
     const int rows_b = min(BN, p.N - n0);
@@ -215,6 +216,9 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
                 for (int j = 0; j < NL; ++j)
                     issue_one(slab_kt(s), s, j, nt);
 
+        // the k-slab of the loads issued in iteration i, computed one iteration
+        // ahead so that the loads after the barrier do not wait for it
+        int kt_next = slab_kt(STAGES - 1);
         for (int i = 0; i < nkt; ++i) {
             const int s = i % STAGES;
             static_assert((STAGES - 2) * NL <= 63, "vmcnt range");
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
                 wait_vmcnt<(STAGES - 2) * NL>();
             wait_lgkmcnt0();
             wg_barrier();
-            const int kt_next = slab_kt(i + STAGES - 1), s_next = (i + STAGES - 1) % STAGES;
+            const int s_next = (i + STAGES - 1) % STAGES;
             if constexpr (EARLY) {
                 if (i + STAGES - 1 < nkt)
 #pragma unroll
@@ -242,6 +246,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
                 if constexpr (!EARLY)
                     issue_one(kt_next, s_next, j, nt);
             });
+            kt_next = slab_kt(i + STAGES);
+            pin_scalar(kt_next);
         }
         // the re-read loads of the last iterations may still be in flight
         if constexpr (!EARLY)

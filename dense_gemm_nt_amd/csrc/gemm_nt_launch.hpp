@@ -14,9 +14,12 @@ typedef hipError_t (*launch_fn)(const KernelArgs &, unsigned grid, hipStream_t);
 // const namespace-scope tables a device copy, leaves these host-only
 typedef launch_fn LaunchTable[2][3];
 
-// kernel-template tiles (gemm_nt_kernel.hpp), in the order of their names
+// kernel-template tiles (gemm_nt_kernel.hpp), in the order of their names,
+// walking K in order and (_rot) in the rotated slab order
 extern LaunchTable kTile128x128_w8_s4, kTile128x128_w8_s4_kmask, kTile128x128_w8_s2,
     kTile32x128_w4_s6;
+extern LaunchTable kTile128x128_w8_s4_rot, kTile128x128_w8_s4_kmask_rot, kTile128x128_w8_s2_rot,
+    kTile32x128_w4_s6_rot;
 // the 256x256 ping-pong kernel (gemm_nt_pp2.hpp), by operand layout: K-major A and B (NT), MN-major B, MN-major A,
 // both MN-major
 extern LaunchTable kPP2_kk, kPP2_km, kPP2_mk, kPP2_mm;

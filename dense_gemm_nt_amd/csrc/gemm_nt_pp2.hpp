@@ -137,7 +137,6 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         const int m0 = tm * BM, n0 = tn * BN;
         const int kt0 = streamk ? sk_kt0 : split * p.kt_per_split;
         const int nk = streamk ? sk_nk : min(p.k_tiles, kt0 + p.kt_per_split) - kt0;
-        const SlabOrder order = slab_order(kt0, nk, p.k_tiles, p.K % BK != 0, n0, streamk ? 0 : p.slab_rot);
 
         const int rows_a = min(BM, p.M - m0);
         const int rows_b = min(BN, p.N - n0);
@@ -176,7 +175,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
             constexpr bool IS_A = decltype(is_a)::value;
             constexpr bool MN = IS_A ? AM : BNM;
             constexpr bool NT = decltype(nt)::value;
-            const int kt = order(i);
+            const int kt = kt0 + i;
             const uint32_t dst = lds0 + (uint32_t)(u * UNIT + (j * 4 + q) * 1024);
             if constexpr (MN) {
                 const uint16_t *X = IS_A ? p.A : p.B;
@@ -236,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         // stored; lane 0's block is always inside N).
         auto scale_load = [&](auto grp, int i) {
             if constexpr (SC == 1) {
-                const int kt = order(i);
+                const int kt = kt0 + i;
                 if constexpr (decltype(grp)::value == 1) {
                     const int m = min(m0 + 64 * q + lane, p.M - 1);
                     const uint32_t v = ((uint32_t)(m >> p.sfa_shift) * (uint32_t)p.sf_ld + (uint32_t)kt) * 4u;
@@ -614,7 +613,6 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_pp2(KernelArgs p0)
         p.rows16 = flags & GD_ROWS16 ? 1 : 0;
         p.bias_vec = flags & GD_BIAS_VEC ? 1 : 0;
         p.nt_b = flags & GD_NT_B ? 1 : 0;
-        p.slab_rot = flags & GD_ROTATE ? 1 : 0;
         if constexpr (F8) {
             p.scale_a = static_cast<const float *>(uptr(d->scale_a));
             p.scale_b = static_cast<const float *>(uptr(d->scale_b));

@@ -206,7 +206,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt0 = split * p.kt_per_split;
     const int nk = min(p.k_tiles, kt0 + p.kt_per_split) - kt0;
-    const SlabOrder order = slab_order(kt0, nk, p.k_tiles, p.K % BK != 0, n0, p.slab_rot);
 
     const int rows_a = min(BM, p.M - m0);
     const int rows_b = min(BN, p.N - n0);
@@ -234,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_w4(KernelArgs p)
     // a unit no later slab reads, which keeps every wait count of the loop the
     // same.  Only the chunks at or past K of a row read zeros.
     auto issue_one = [&](int op, int i, int u, int j, auto nt) {
-        const int kt = order(i < nk ? i : nk - 1);
+        const int kt = kt0 + (i < nk ? i : nk - 1);
         const bool kin = lc * 8 < p.K - kt * BK;
         const uint32_t kb = (uint32_t)kt * (uint32_t)(BK * 2);
         const int row = 32 * j + 8 * wave + lr;

@@ -78,10 +78,10 @@ typedef enum {
  * names no configuration makes gemm_create return GEMM_ERR_INVALID_ARG.
  * GEMM_PERSIST=1 runs planned 256 x 256 ping-pong grids of more than 256
  * blocks with 256 persistent blocks.  GEMM_ROTATE=0/1/2 sets the order in
- * which tiles walk their K slabs: every tile from its first slab, a start
- * rotated per 256-column block when M <= 128 (default), or rotated always; the
- * order changes the FP32 summation order, so the bits of a shape depend on
- * this switch and on nothing else of the plan's.  GEMM_LOG=1 prints each call's plan to
+ * which the 32 x 128 and 128 x 128 tiles walk their K slabs: from the first
+ * slab, from a start rotated per 256-column block when M <= 128 (default), or
+ * rotated always (the 256-row tiles always start at the first slab); the
+ * order is the FP32 summation order, so it changes the bits.  GEMM_LOG=1 prints each call's plan to
  * stderr.  GEMM_TEST_FAIL_ALLOC=1 makes gemm_create fail as a failed workspace
  * allocation does (GEMM_ERR_ALLOC, *out NULL), to test callers' error paths. */
 gemm_status_t gemm_create(gemm_handle_t *out);

@@ -149,8 +149,9 @@ def test_every_family_is_built(kernels):
         fams.setdefault(_family(n), []).append(n)
     assert None not in fams, fams.get(None)
     # tile kernels: 128x128 with 4 stages, 4 stages K-masked and 2 stages, and
-    # 32x128; 2 in x 3 out types each
-    assert len(fams["gemm_nt_kernel"]) == 4 * 6
+    # 32x128; 2 in x 3 out types each, in the natural and the rotated k-slab order
+    assert len(fams["gemm_nt_kernel"]) == 4 * 6 * 2
+    assert sum(_args(n)[-1] for n in fams["gemm_nt_kernel"]) == 4 * 6
     # ping-pong: NT, three MN-major layouts, grouped, persistent (2 x 3 each);
     # stream-K (2); FP8: 4 type pairs x 2 scale modes x 3 out, plain and grouped
     assert len(fams["gemm_nt_pp2"]) == 6 * 6 + 2 + 4 * 2 * 3 * 2
@@ -182,7 +183,7 @@ def test_lds_and_register_budget(kernels):
         assert per_simd * k[".vgpr_count"] <= REGS_PER_SIMD_LANE, (n, per_simd, k[".vgpr_count"])
     # the two-stage 128x128 tile is the one meant to run two blocks per unit
     two = [n for n in kernels if _family(n) == "gemm_nt_kernel" and _args(n)[5] == 2]
-    assert len(two) == 6
+    assert len(two) == 2 * 6
     for n in two:
         assert LDS_BYTES // kernels[n][".group_segment_fixed_size"] >= 2, n
 

@@ -70,25 +70,6 @@ def test_fp8_every_element(fa, fb, mode, block_m, out_dt):
 
 
 @pytest.mark.parametrize("mode,block_m", SCALINGS)
-@pytest.mark.parametrize("splits", [None, 2])
-def test_fp8_rotated_slab_order(mode, block_m, splits):
-    # FP8 k-slabs (128 deep) in the rotated order (GEMM_ROTATE=2), the
-    # blockwise scales following their slab: K = 1040 is 8 slabs and a 16-deep
-    # partial last one, which keeps its place; three 256-column blocks, so
-    # three different starts.  Both orders within the oracle's bound.
-    M, N, K = 100, 600, 1040
-    say("case fp8 rotated order %s/%d splits=%s" % (mode, block_m, splits))
-    A, B, sa, sb = make_fp8_operands(M, N, K, "e4m3", "e4m3", "uniform", seed=8, mode=mode,
-                                     block_m=block_m, lda=K + 16, ldb=K + 16)
-    Cr, S = _oracle(A, B, sa, sb, K, "e4m3", "e4m3", mode, block_m)
-    for rotate in (0, 2):
-        h = new_handle(None, splits, rotate=rotate)
-        C = _run(h, A, B, sa, sb, K, "e4m3", "e4m3", mode, block_m, "fp32")
-        h.close()
-        check(C, Cr, S, "fp32", "fp8 %s rotate=%d" % (mode, rotate))
-
-
-@pytest.mark.parametrize("mode,block_m", SCALINGS)
 @pytest.mark.parametrize("splits", [None, 3])
 def test_fp8_small_integers_bitwise(mode, block_m, splits):
     M, N, K = 300, 264, 512

@@ -98,10 +98,11 @@ def test_layout_unaligned_ldc(la, lb, out_dt, pad):
 @pytest.mark.parametrize("la,lb", [("k", "k")] + OTHER)
 @pytest.mark.parametrize("splits", [None, 2])
 def test_layout_rotated_slab_order(la, lb, splits):
-    # k-slabs in the rotated order (GEMM_ROTATE=2) on every layout: K = 1000 is
-    # 15 slabs of 64 and a partial last one, which keeps its place; 600
-    # columns are three 256-column blocks, so three different starts.  Random
-    # values against the oracle, and small integers bitwise against the
+    # GEMM_ROTATE=2 on every layout: K-major operands run on the 128x128 tile
+    # in the rotated k-slab order (K = 1000 is 15 slabs of 64 and a partial
+    # last one, which keeps its place; 600 columns are three 256-column blocks,
+    # so three different starts), MN-major ones on the ping-pong tile, in order.
+    # Random values against the oracle, and small integers bitwise against the
     # natural order (exact sums, so any order gives the same bits).
     M, N, K = 100, 600, 1000
     say("case layout rotated order %s%s splits=%s" % (la, lb, splits))
