@@ -90,15 +90,15 @@ SWEEPS = {
          (3000, 3000, 5000, "fp16", "fp32", "uniform")],
         [("plan", {}), (W4_256x128, {"GEMM_CONFIG": W4_256x128})]),
     "slab_rotation": (
-        "each 256-column block of tiles starting its k-slabs at a rotated slab when M <= 128, "
-        "against every tile walking K from its first slab, and against rotation at every M",
-        [(256, 28672, 8192, "bf16", "bf16", "llm"), (256, 8192, 28672, "bf16", "bf16", "llm"),
-         (256, 10240, 8192, "bf16", "bf16", "llm"), (256, 8192, 8192, "bf16", "bf16", "llm"),
-         (1, 8192, 8192, "bf16", "bf16", "llm"), (32, 8192, 8192, "bf16", "bf16", "llm"),
-         (1, 4096, 16384, "bf16", "bf16", "llm"), (127, 28672, 8192, "fp16", "fp32", "uniform"),
-         (512, 8192, 8192, "bf16", "bf16", "llm"), (4096, 4096, 4096, "bf16", "bf16", "uniform"),
-         (8192, 8192, 8192, "bf16", "bf16", "uniform"), (8192, 28672, 8192, "bf16", "bf16", "llm"),
-         (1000, 4097, 1536, "fp16", "fp32", "uniform"), (2048, 2048, 2048, "bf16", "fp32", "uniform")],
+        "the 32x128 and 128x128 tiles: each 256-column block of tiles starting its k-slabs at a "
+        "rotated slab when M <= 128, against walking K from the first slab, and against rotation "
+        "at every M (the 256-row tiles always walk K in order)",
+        [(1, 8192, 8192, "bf16", "bf16", "llm"), (32, 8192, 8192, "bf16", "bf16", "llm"),
+         (64, 8192, 8192, "bf16", "bf16", "llm"), (1, 4096, 16384, "bf16", "bf16", "llm"),
+         (1, 2048, 32768, "bf16", "bf16", "llm"), (96, 8192, 8192, "bf16", "bf16", "llm"),
+         (128, 8192, 8192, "bf16", "bf16", "llm"), (127, 28672, 8192, "fp16", "fp32", "uniform"),
+         (1024, 1024, 1024, "bf16", "fp32", "uniform"), (1000, 4097, 1536, "fp16", "fp32", "uniform"),
+         (1500, 2900, 1024, "bf16", "bf16", "uniform"), (2048, 2048, 2048, "bf16", "fp32", "uniform")],
         [("plan", {}), ("natural order", {"GEMM_ROTATE": "0"}), ("rotated", {"GEMM_ROTATE": "2"})]),
     "in_kernel_reduction": (
         "two K splits on the 256-row tiles: the second split to finish adds the "
