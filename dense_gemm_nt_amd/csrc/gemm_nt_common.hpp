@@ -97,11 +97,14 @@ struct KernelArgs {
 // share their low bits, and the requests load a few memory channels only.  A
 // streaming probe of a decode-shaped B operand (28672 rows of 16 KB, 224
 // blocks reading 128 bytes of 256 rows per step) reached 4.7 TB/s in step and
-// 6.1 TB/s with the starts rotated.  The slab sum is the same sum in another
-// order, fixed by an output's 256-column block and its split's range: every
-// launch of a shape gives the same bits.  Without ROT, slab kt0 + i: the
-// order is a template parameter because its few scalar instructions per slab
-// measured about 1% on the large shapes, which never rotate.
+// 6.1 TB/s with the starts rotated when consecutive blocks took consecutive
+// tiles, and 5.6-5.8 against 6.0 in the kernels' XCD-aware block order; in the
+// small-M tile kernels rotation measured 5-25% faster (the host's rule,
+// rotate_slabs, also says why the 256-row tiles never rotate).  The slab sum
+// is the same sum in another order, fixed by an output's 256-column block and
+// its split's range: every launch of a shape gives the same bits.  Without
+// ROT, slab kt0 + i: the order is a template parameter because its few scalar
+// instructions per slab measured about 1% on the large shapes.
 template <bool ROT>
 struct SlabOrder {
     int kt0, nf, rot;
