@@ -284,13 +284,15 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         p.group_m = 1;
     p.grid = tiles * splits;
     p.ws_bytes = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
-    // Two K splits on the 256-row tiles: the second split to finish adds the
-    // first's partial (one 256 x BN FP32 slot per split and tile) and stores
+    // Two K splits on the 256-row tiles, any number on the tile kernels with a
+    // ring deeper than two stages: the last split of a tile to finish adds the
+    // others' partials (one BM x BN FP32 slot per split and tile) and stores
     // the tile, instead of a second pass over [splits][M][N] partials.
-    if (inreduce && splits == 2 &&
-        (cfg == CFG_PP2_256x256 || cfg == CFG_W4_256x128) &&
+    const bool many = cfg != CFG_PP2_256x256 && cfg != CFG_W4_256x128 && c.stages > 2;
+    const bool two = cfg == CFG_PP2_256x256 || cfg == CFG_W4_256x128;
+    if (inreduce && ((splits == 2 && two) || (splits >= 2 && many)) &&
         tiles * 4 <= GEMM_COUNTER_BYTES) {
-        const int64_t need = tiles * 2 * (int64_t)c.bm * c.bn * 4;
+        const int64_t need = tiles * splits * (int64_t)c.bm * c.bn * 4;
         if (need <= ws_bytes) {
             p.inreduce = 1;
             p.ws_bytes = need;

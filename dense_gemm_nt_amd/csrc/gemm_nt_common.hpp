@@ -361,6 +361,98 @@ __device__ __forceinline__ bool splitk2_arrive(const KernelArgs &p, f32x16 (&acc
     return true;
 }
 
+// Any number S = p.splits >= 2 of K splits reduced inside the kernel, by the
+// last of a tile's splits to finish (the tile kernels; the same exchange as
+// splitk2_arrive).  Each split stores its FP32 partial in register order into
+// slot `split` of the tile's S slots with device-coherent stores, waits for
+// them and counts its arrival on counters[tile].  The split that counts last
+// adds the partials in split order, ((0 + p_0) + p_1) + ..., its own from its
+// registers and the others' with device-coherent loads, the loads of RS splits
+// in flight at a time.  That is the order, hence the bits, of the second pass
+// (splitk_sum), whichever split came last.  It resets the counter for the
+// next call and returns true; the others return false and are done.  No block
+// waits for another.  `flag` is a word of LDS no wave is using.
+template <int NW, int FN, int FM>
+__device__ __forceinline__ bool splitk_arrive(const KernelArgs &p, f32x16 (&acc)[FN][FM], int tile, int split,
+                                              int wave, int lane, uint32_t *flag)
+{
+    constexpr int G = FN * FM * 4;                        // register groups per lane
+    constexpr uint32_t SLOT = (uint32_t)NW * G * 1024u;   // bytes per split partial
+    constexpr int SC1 = 16;                               // device-coherent access
+    constexpr int RS = G >= 16 ? 1 : 16 / G;              // splits read per round
+    const int S = p.splits;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const uint8_t *>(p.partials) + (int64_t)tile * S * SLOT, (uint32_t)S * SLOT);
+    const uint32_t vo = (uint32_t)(wave * G) * 1024u + (uint32_t)lane * 16u;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int g = (fn * FM + fm) * 4 + q;
+                const f32x4 v = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                 acc[fn][fm][4 * q + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, vo + g * 1024u,
+                                                       (uint32_t)split * SLOT, SC1);
+            }
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (wave == 0 && lane == 0)
+        *flag = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wg_barrier();
+    const uint32_t arrived = __builtin_amdgcn_readfirstlane(*flag);
+    wg_barrier();                                         // every wave has read the flag
+    if (arrived != (uint32_t)(S - 1))
+        return false;
+    f32x4 tot[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        tot[g] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < S; s0 += RS) {
+        f32x4 buf[RS][G];
+#pragma unroll
+        for (int c = 0; c < RS; ++c) {
+            const int s = s0 + c;
+            if (s < S && s != split) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    buf[c][g] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo + g * 1024u, (uint32_t)s * SLOT, SC1));
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < RS; ++c) {
+            const int s = s0 + c;
+            if (s >= S)
+                continue;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int g = (fn * FM + fm) * 4 + q;
+                        const f32x4 own = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                           acc[fn][fm][4 * q + 3]};
+                        tot[g] += s == split ? own : buf[c][g];
+                    }
+        }
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[fn][fm][4 * q + e] = tot[(fn * FM + fm) * 4 + q][e];
+    if (wave == 0 && lane == 0)
+        __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
 template <int OUT>
 __device__ __forceinline__ void store4(void *C, int64_t idx, f32x4 v, bool vec, int valid)
 {

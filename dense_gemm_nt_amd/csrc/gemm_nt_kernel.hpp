@@ -72,7 +72,10 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
     const int wave_m = wave / WN, wave_n = wave % WN;
 
     int tm, tn, split;
-    map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+    if (p.inreduce)       // the K splits of a tile adjacent in launch order (splitk_arrive)
+        map_block_split_minor(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, tm, tn, split);
+    else
+        map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
     const int tile = tm * p.tiles_n + tn;
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt_begin = split * p.kt_per_split;
@@ -258,6 +261,20 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_nt_kernel(KernelArgs p)
             main_loop(std::true_type{});
         else
             main_loop(std::false_type{});
+    }
+
+    // K splits reduced here: the last split of the tile to finish adds the
+    // others' partials and stores the tile as an unsplit one (the flag word is
+    // in the ring, which no wave reads any more once the partials are stored).
+    // Not in the two-stage ring, which runs two blocks per compute unit and
+    // has no registers for the reduction's buffers.
+    if constexpr (STAGES > 2) {
+        if (p.inreduce) {
+            if (!splitk_arrive<NWAVES, FN, FM>(p, acc, tile, split, wave, lane,
+                                               reinterpret_cast<uint32_t *>(smem)))
+                return;
+            p.splits = 1;
+        }
     }
 
     // Epilogue without a fused epilogue: each wave's block through its share of

@@ -121,7 +121,11 @@ def test_plans_fit_the_machine(g, M, N, K):
         return
     assert p["workgroups"] == p["tiles"] * p["splits"]
     assert 1 <= p["splits"] <= max(1, k_tiles)
-    if p["splits"] > 1:
+    if p["splits"] > 1 and p["inreduce"]:
+        # reduced in the kernel: one BM x BN FP32 slot per tile and split
+        assert p["workspace_bytes"] == p["tiles"] * p["splits"] * bm * bn * 4
+        assert p["workspace_bytes"] <= 128 << 20
+    elif p["splits"] > 1:
         assert p["workspace_bytes"] == p["splits"] * M * N * 4
         assert p["workspace_bytes"] <= 128 << 20
     else:

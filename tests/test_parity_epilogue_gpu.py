@@ -69,7 +69,8 @@ EPIS = [
 
 
 @pytest.mark.parametrize("config,splits", [("256x256x64_w8_pp2", None), ("128x128x64_w8_s4", None),
-                                           ("256x256x64_w8_pp2", 3), ("32x128x64_w4_s6", None)])
+                                           ("256x256x64_w8_pp2", 3), ("32x128x64_w4_s6", None),
+                                           ("32x128x64_w4_s6", 3), ("128x128x64_w8_s4", 2)])
 @pytest.mark.parametrize("alpha,beta,along,act", EPIS)
 @pytest.mark.parametrize("out_dt", ["bf16", "fp32"])
 def test_epilogue_every_element(config, splits, alpha, beta, along, act, out_dt):

@@ -90,3 +90,51 @@ def test_fused_epilogue_after_in_kernel_reduction():
         aS, t = oepi.scale_of(S, alpha=1.5, bias=bias.numpy().astype(np.float64), bias_along="n")
         check_epilogue(C.float().cpu().double().numpy(), D, aS, t, "bf16", config)
         h.close()
+
+
+# Any number of K splits on the tile kernels (32x128, 128x128 with four
+# stages, K-masked): the last split of a tile to finish adds the others'
+# partials in split order, so every result must be bitwise the second pass's
+# (GEMM_INREDUCE=0), whichever split came last, and stay so over repeated
+# calls (the counters go back to zero).
+T32, T128, KMASK = "32x128x64_w4_s6", "128x128x64_w8_s4", "128x128x64_w8_s4_kmask"
+
+
+@pytest.mark.parametrize("config,splits,M,N,K,outd", [
+    (T32, 2, 64, 1000, 2048, "bf16"), (T32, 3, 1, 8192, 8192, "bf16"), (T32, 5, 20, 1000, 4104, "fp16"),
+    (T32, 6, 16, 4096, 16384, "bf16"), (T32, 12, 1, 2048, 32768, "fp32"), (T32, 7, 33, 300, 1800, "fp32"),
+    (T128, 2, 128, 2100, 1024, "bf16"), (T128, 4, 96, 8192, 8192, "bf16"), (T128, 3, 127, 3000, 2056, "fp32"),
+    (KMASK, 3, 90, 700, 1001, "bf16")])
+def test_tile_kernel_splits_equal_second_pass_bitwise(config, splits, M, N, K, outd):
+    say("case tile in-kernel %d splits vs second pass %s M=%d N=%d K=%d ->%s" % (splits, config, M, N, K, outd))
+    ld = -(-K // 8) * 8
+    A, B = make_operands(M, N, K, "bf16", "llm", seed=K + splits, lda=ld, ldb=ld)
+    h1 = new_handle(config, splits, inreduce=1)
+    h0 = new_handle(config, splits, inreduce=0)
+    C1 = run_gpu(h1, A, B, K, "bf16", outd)
+    C0 = run_gpu(h0, A, B, K, "bf16", outd)
+    assert np.array_equal(C1, C0)
+    for _ in range(2):
+        assert np.array_equal(run_gpu(h1, A, B, K, "bf16", outd), C1)
+    if M * N * K <= 2 ** 31:
+        compare_full(C1, A, B, K, "bf16", outd, "tile in-kernel %d splits" % splits)
+    h1.close()
+    h0.close()
+
+
+def test_tile_kernel_splits_small_integers_bitwise():
+    M, N, K, splits = 40, 1100, 5000, 9
+    say("case tile in-kernel int3 %d splits M=%d N=%d K=%d" % (splits, M, N, K))
+    A, B = make_operands(M, N, K, "bf16", "int3", seed=9)
+    Cr, _ = oracle.gemm_nt(A, B, K=K, in_dtype="bf16")
+    h = new_handle(T32, splits, inreduce=1)
+    for _ in range(2):
+        assert np.array_equal(run_gpu(h, A, B, K, "bf16", "fp32"), Cr)
+    h.close()
+
+
+def test_default_small_m_plans_reduce_in_kernel():
+    import dense_gemm_nt_amd as g
+    for M, N, K in [(1, 8192, 8192), (32, 8192, 8192), (1, 4096, 16384), (96, 8192, 8192)]:
+        p = g.gemm_plan(M, N, K, 0, 0)
+        assert p["splits"] > 1 and p["inreduce"] == 1, (M, N, K, p)
