@@ -165,10 +165,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     } else if (K % 8) {
         cfg = CFG_T128x128_KMASK;
     } else if (M <= 64) {
-        // (at M = 64, two 32-row tiles per column still beat one 128-row tile:
-        // 39.2 -> 36.8 us at 64x8192x8192, 19.9 -> 15.3 at 64x4096x4096; from
-        // M = 96 the 128x128 tile is faster by half)
-        cfg = CFG_T32x128;
+        // The 32x128 tile, while its tiles fit one pass of the machine: two
+        // 32-row tiles per column still beat one 128-row tile at 64 x 4096 x
+        // 4096 (15.3 against 20.8 us) and are level with it at 40 x 8192 x 8192
+        // (32.3 against 32.5).  Past one pass (M > 32 over N > 16384) the
+        // second, mostly empty pass costs more than the 128-row tile's idle
+        // rows: 40 x 28672 x 8192 73.9 against 103.2 us, 64 x 28672 x 8192 77.0
+        // against 110.9.  From M = 96 the 128x128 tile is faster by half.
+        cfg = M <= 32 || cdiv(M, 32) * cdiv(N, 128) <= kNumCUs ? CFG_T32x128 : CFG_T128x128;
     } else if (M <= 128) {
         cfg = CFG_T128x128;
     } else if (M <= 256) {

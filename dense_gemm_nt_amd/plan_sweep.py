@@ -37,8 +37,11 @@ SWEEPS = {
          (256, 28672, 8192, "bf16", "bf16", "llm"), (256, 8192, 28672, "bf16", "bf16", "llm")],
         [("plan", {}), (PP2, {"GEMM_CONFIG": PP2}), (W4_256x128, {"GEMM_CONFIG": W4_256x128})]),
     "small_m": (
-        "M <= 64: the 32x128 tile; from M = 96 the 128x128 tile",
-        [(m, 8192, 8192, "bf16", "bf16", "llm") for m in (1, 16, 32, 64, 96, 128)],
+        "M <= 64: the 32x128 tile while its tiles fit one pass of the machine (M <= 32 always); "
+        "from M = 96, or past one pass, the 128x128 tile",
+        [(m, 8192, 8192, "bf16", "bf16", "llm") for m in (1, 16, 32, 64, 96, 128)] +
+        [(40, 28672, 8192, "bf16", "bf16", "llm"), (64, 28672, 8192, "bf16", "bf16", "llm"),
+         (32, 28672, 8192, "bf16", "bf16", "llm"), (64, 4096, 4096, "bf16", "bf16", "llm")],
         [("plan", {}), (T32, {"GEMM_CONFIG": T32}), (T128, {"GEMM_CONFIG": T128})]),
     "small_square": (
         "small squares: the 32x128 tile when it fills at least as many compute units "
@@ -101,9 +104,12 @@ SWEEPS = {
          (1500, 2900, 1024, "bf16", "bf16", "uniform"), (2048, 2048, 2048, "bf16", "fp32", "uniform")],
         [("plan", {}), ("natural order", {"GEMM_ROTATE": "0"}), ("rotated", {"GEMM_ROTATE": "2"})]),
     "in_kernel_reduction": (
-        "two K splits on the 256-row tiles: the second split to finish adds the "
-        "first's partial, instead of a second pass",
-        [(256, 28672, 8192, "bf16", "bf16", "llm"), (512, 8192, 8192, "bf16", "bf16", "llm")],
+        "K splits reduced in the kernel by the last split of a tile to finish (two on the "
+        "256-row tiles, any number on the 32x128 and 128x128 tiles), instead of a second pass",
+        [(256, 28672, 8192, "bf16", "bf16", "llm"), (512, 8192, 8192, "bf16", "bf16", "llm"),
+         (1, 8192, 8192, "bf16", "bf16", "llm"), (16, 4096, 4096, "bf16", "bf16", "llm"),
+         (1, 2048, 32768, "bf16", "bf16", "llm"), (64, 8192, 8192, "bf16", "bf16", "llm"),
+         (96, 8192, 8192, "bf16", "bf16", "llm"), (128, 8192, 8192, "bf16", "bf16", "llm")],
         [("plan", {}), ("second pass", {"GEMM_INREDUCE": "0"})]),
 }
 

@@ -172,10 +172,17 @@ def test_plan_regimes(g):
                           ((1, 16384, 8192), 3), ((1, 6144, 8192), 3)):
         p = g.gemm_plan(M, N, K)
         assert p["name"] == "32x128x64_w4_s6" and p["splits"] == sp, (M, N, K, p)
-    # M = 64 (two tile rows sharing B) still fills every compute unit
+    # M = 64 (two tile rows sharing B) still fills every compute unit, and
+    # reduces its splits in the kernel
     p = g.gemm_plan(64, 8192, 8192)
     assert p["name"] == "32x128x64_w4_s6" and p["splits"] == 2 and p["workgroups"] == 256
+    assert p["inreduce"] == 1 and p["workspace_bytes"] == p["tiles"] * 2 * 32 * 128 * 4
     assert g.gemm_plan(96, 28672, 8192)["name"] == "128x128x64_w8_s4"
+    # 32 < M <= 64: the 32x128 tile only while its tiles fit one pass
+    assert g.gemm_plan(32, 28672, 8192)["name"] == "32x128x64_w4_s6"
+    for M in (33, 40, 64):
+        assert g.gemm_plan(M, 28672, 8192)["name"] == "128x128x64_w8_s4", M
+        assert g.gemm_plan(M, 16384, 8192)["name"] == "32x128x64_w4_s6", M
     # two K splits on the 256-row tiles are reduced inside the kernel (one
     # 256 x 256 FP32 slot per split and tile); more splits take the second pass
     p = g.gemm_plan(256, 28672, 8192)
