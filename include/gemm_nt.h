@@ -69,8 +69,10 @@ typedef enum {
 /* Create a handle on the current device: allocates the workspace for split-K
  * and stream-K partials (128 MiB by default; GEMM_WORKSPACE_MB overrides) and
  * 64 KiB of per-tile counters, which it zeroes (synchronously) and which every
- * call leaves at zero.  GEMM_INREDUCE=0 turns the in-kernel reduction of two
- * K splits off (every split plan then takes the second pass).
+ * call leaves at zero.  GEMM_INREDUCE=0 turns the in-kernel reduction of K
+ * splits off (two on the 256-row tiles, any number on the 32 x 128 and
+ * 128 x 128 tiles; every split plan then takes the second pass, with the
+ * same bits).
  * *out is NULL on error.  For measurement, GEMM_CONFIG=<name> forces one kernel
  * configuration, GEMM_SPLITS=<n> a K split on every call of this handle, and
  * GEMM_STREAMK=0/1/2 turns stream-K off, leaves it to the plan (default) or
