@@ -185,11 +185,40 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         // i.e. half the FP32 partial traffic (interleaved medians: 59.5 -> 56.6,
         // 53.0 -> 50.0, 126.2 -> 123.0 us; with two splits, at 256 x 28672 x
         // 8192, the ping-pong tile stays faster: 122.6 against 126.1 us).
+        //
+        // Either 256-row tile only while its blocks fill the machine as well
+        // as the 128x128 tile's would (the fraction of the passes they fill,
+        // with the K splits the split rule below gives each): with short K or
+        // few N tiles the 256-row tiles' splits (at least 20 slabs each) leave
+        // most compute units idle.  Interleaved medians: 192 x 4096 x 4096
+        // 22.4 us on the 128x128 tile against 42.8 on the ping-pong tile,
+        // 200 x 6144 x 3072 24.3 against 55.1, 256 x 8192 x 2048 21.7 against
+        // 41.6, 256 x 2048 x 8192 26.5 against 33.9 on the four-wave tile; and
+        // the four-wave tile over the ping-pong one when it fills more
+        // (256 x 16384 x 4096: 45.3 against 53.0 us), or as much while the
+        // ping-pong tile's splits would hold fewer than 64 slabs each
+        // (256 x 28672 x 4096: 62.7 against 67.1 us; at K = 8192, 64 slabs
+        // per split, the ping-pong tile: 121.8 against 124.3).
         cfg = CFG_PP2_256x256;
         const int64_t t256 = cdiv(N, 256), kt64 = cdiv(K, 64);
         const int64_t s256 = std::min<int64_t>(kNumCUs / std::max<int64_t>(1, t256), kt64 / 20);
-        if (t256 < kNumCUs && s256 > 4)
+        auto blocks = [&](int64_t tiles, int64_t min_slabs) {
+            int64_t s = 1;
+            if (tiles < kNumCUs && kt64 >= 16)
+                s = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / tiles, kt64 / min_slabs));
+            return tiles * s;
+        };
+        auto fill = [](int64_t b) { return (double)b / (double)(cdiv(b, kNumCUs) * kNumCUs); };
+        const int64_t b_w4 = blocks(cdiv(N, 128), 20), b_128 = blocks(cdiv(M, 128) * cdiv(N, 128), 8);
+        const int64_t b_pp2 = blocks(t256, 20);
+        double f = fill(b_pp2);
+        const bool short_splits = kt64 * t256 / b_pp2 < 64;
+        if (t256 < kNumCUs && (s256 > 4 || fill(b_w4) > f || (fill(b_w4) == f && short_splits))) {
             cfg = CFG_W4_256x128;
+            f = fill(b_w4);
+        }
+        if (fill(b_128) > f)
+            cfg = CFG_T128x128;
     } else {
         // The 256x256 ping-pong tile when its blocks fill at least half the
         // machine, with the K splits the split rule below would give it (at

@@ -36,6 +36,16 @@ SWEEPS = {
         [(256, 10240, 8192, "bf16", "bf16", "llm"), (256, 8192, 8192, "bf16", "bf16", "llm"),
          (256, 28672, 8192, "bf16", "bf16", "llm"), (256, 8192, 28672, "bf16", "bf16", "llm")],
         [("plan", {}), (PP2, {"GEMM_CONFIG": PP2}), (W4_256x128, {"GEMM_CONFIG": W4_256x128})]),
+    "decode_fill": (
+        "128 < M <= 256: a 256-row tile only while its blocks fill the machine as well as the "
+        "128x128 tile's would; the four-wave tile over the ping-pong tile when it fills more",
+        [(192, 4096, 4096, "bf16", "bf16", "llm"), (256, 4096, 4096, "bf16", "bf16", "llm"),
+         (256, 8192, 2048, "bf16", "bf16", "llm"), (256, 2048, 8192, "bf16", "bf16", "llm"),
+         (200, 6144, 3072, "bf16", "bf16", "llm"), (256, 8192, 4096, "bf16", "bf16", "llm"),
+         (256, 16384, 4096, "bf16", "bf16", "llm"), (256, 28672, 4096, "bf16", "bf16", "llm"),
+         (160, 4096, 8192, "bf16", "bf16", "llm")],
+        [("plan", {}), (T128, {"GEMM_CONFIG": T128}), (W4_256x128, {"GEMM_CONFIG": W4_256x128}),
+         (PP2, {"GEMM_CONFIG": PP2})]),
     "small_m": (
         "M <= 64: the 32x128 tile while its tiles fit one pass of the machine (M <= 32 always); "
         "from M = 96, or past one pass, the 128x128 tile",

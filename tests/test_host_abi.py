@@ -196,6 +196,13 @@ def test_plan_regimes(g):
         assert p["name"] == "256x128x64_w4_u8" and p["splits"] in (3, 4), p
         assert p["inreduce"] == 0 and p["workspace_bytes"] == p["splits"] * 256 * N * 4
     assert g.gemm_plan(256, 28672, 8192)["name"] == "256x256x64_w8_pp2"
+    # 128 < M <= 256 with short K or few N tiles: the 256-row tiles only while
+    # they fill the machine as well as the 128x128 tile
+    for M, N, K in ((192, 4096, 4096), (256, 8192, 2048), (256, 2048, 8192), (200, 6144, 3072)):
+        assert g.gemm_plan(M, N, K)["name"] == "128x128x64_w8_s4", (M, N, K)
+    assert g.gemm_plan(256, 16384, 4096)["name"] == "256x128x64_w4_u8"
+    # as full as the ping-pong tile, whose two splits would hold 32 slabs each
+    assert g.gemm_plan(256, 28672, 4096)["name"] == "256x128x64_w4_u8"
     # more than two splits on the ping-pong tile take the second pass
     p = g.gemm_plan(512, 8192, 8192)
     assert p["name"] == "256x256x64_w8_pp2" and p["splits"] == 4 and p["inreduce"] == 0

@@ -23,13 +23,16 @@ def _shapes():
         # (M range, N range, K range): small M with long K (K splits); small
         # squares; 96 < M <= 128 (128x128 tile with K splits); 128x128 tiles
         # just past one pass of the machine (two blocks per compute unit);
-        # decode-like 128 < M <= 256 (ping-pong tile, K splits); mid squares
+        # 128 < M <= 256 with few N tiles (128x128 tile, K splits); mid
+        # squares; 128 < M <= 256 with many N tiles (ping-pong tile, K splits)
         ((1, 64), (100, 1200), (1024, 4096)),
         ((257, 700), (257, 700), (64, 1100)),
         ((97, 128), (2000, 6000), (512, 2048)),
         ((990, 1020), (4100, 4300), (256, 512)),
         ((129, 256), (300, 1500), (2048, 6000)),
         ((1500, 2100), (1500, 2100), (256, 768)),
+        # decode-like with many N tiles: the ping-pong tile with two K splits
+        ((129, 256), (14000, 18000), (6000, 8200)),
     ]
     out = []
     for (m0, m1), (n0, n1), (k0, k1) in regimes:
