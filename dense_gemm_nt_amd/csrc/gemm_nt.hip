@@ -160,6 +160,17 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
 {
     Plan p{};
     int cfg;
+    // A tile family's blocks with the K splits the split rule below would give
+    // it (at least min_slabs 64-deep slabs each), and the fraction of their
+    // passes of the machine they fill.
+    const int64_t kt64 = cdiv(K, 64);
+    auto blocks = [&](int64_t tiles, int64_t min_slabs) {
+        int64_t s = 1;
+        if (tiles < kNumCUs && kt64 >= 16)
+            s = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / tiles, kt64 / min_slabs));
+        return tiles * s;
+    };
+    auto fill = [](int64_t b) { return (double)b / (double)(cdiv(b, kNumCUs) * kNumCUs); };
     if (force_cfg >= 0) {
         cfg = force_cfg;
     } else if (K % 8) {
@@ -200,15 +211,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         // (256 x 28672 x 4096: 62.7 against 67.1 us; at K = 8192, 64 slabs
         // per split, the ping-pong tile: 121.8 against 124.3).
         cfg = CFG_PP2_256x256;
-        const int64_t t256 = cdiv(N, 256), kt64 = cdiv(K, 64);
+        const int64_t t256 = cdiv(N, 256);
         const int64_t s256 = std::min<int64_t>(kNumCUs / std::max<int64_t>(1, t256), kt64 / 20);
-        auto blocks = [&](int64_t tiles, int64_t min_slabs) {
-            int64_t s = 1;
-            if (tiles < kNumCUs && kt64 >= 16)
-                s = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / tiles, kt64 / min_slabs));
-            return tiles * s;
-        };
-        auto fill = [](int64_t b) { return (double)b / (double)(cdiv(b, kNumCUs) * kNumCUs); };
         const int64_t b_w4 = blocks(cdiv(N, 128), 20), b_128 = blocks(cdiv(M, 128) * cdiv(N, 128), 8);
         const int64_t b_pp2 = blocks(t256, 20);
         double f = fill(b_pp2);
@@ -226,6 +230,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         const int64_t big = std::max<int64_t>(1, cdiv(M, 256) * cdiv(N, 256));
         const int64_t ksplit = std::min<int64_t>(kNumCUs / big, cdiv(K, 64) / 20);
         cfg = big * std::max<int64_t>(1, ksplit) >= kNumCUs / 2 ? CFG_PP2_256x256 : CFG_T128x128;
+        // ... and the 128x128 tile even then, when its tiles fit one pass and
+        // fill it at least as well (640 x 2048 x 8192: 37.9 against 50.6 us;
+        // 768 x 4096 x 4096 40.9 against 44.5; 384 x 8192 x 4096 41.9 against
+        // 45.6).  Its plans past one pass (the two-stage ring) measured mixed
+        // against the ping-pong tile and keep the rule above.
+        const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
+        if (cfg == CFG_PP2_256x256 && t128 < kNumCUs && fill(blocks(t128, 8)) >= fill(blocks(big, 20)))
+            cfg = CFG_T128x128;
         // Small squares: the 32x128 tile, when without K splits it fills at
         // least as many compute units (in one pass) as the 128x128 tile does with
         // the splits the rule below gives it; it then needs no partials.

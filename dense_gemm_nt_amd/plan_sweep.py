@@ -46,6 +46,13 @@ SWEEPS = {
          (160, 4096, 8192, "bf16", "bf16", "llm")],
         [("plan", {}), (T128, {"GEMM_CONFIG": T128}), (W4_256x128, {"GEMM_CONFIG": W4_256x128}),
          (PP2, {"GEMM_CONFIG": PP2})]),
+    "mid_fill": (
+        "M > 256: the 128x128 tile, where its tiles fit one pass, when it fills that pass at "
+        "least as well as the ping-pong tile fills its own",
+        [(768, 4096, 4096, "bf16", "bf16", "llm"), (384, 8192, 4096, "bf16", "bf16", "llm"),
+         (640, 2048, 8192, "bf16", "bf16", "llm"), (512, 16384, 2048, "bf16", "bf16", "llm"),
+         (512, 8192, 8192, "bf16", "bf16", "llm"), (768, 8192, 2048, "bf16", "bf16", "llm")],
+        [("plan", {}), (T128, {"GEMM_CONFIG": T128}), (PP2, {"GEMM_CONFIG": PP2})]),
     "small_m": (
         "M <= 64: the 32x128 tile while its tiles fit one pass of the machine (M <= 32 always); "
         "from M = 96, or past one pass, the 128x128 tile",

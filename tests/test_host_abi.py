@@ -201,6 +201,11 @@ def test_plan_regimes(g):
     for M, N, K in ((192, 4096, 4096), (256, 8192, 2048), (256, 2048, 8192), (200, 6144, 3072)):
         assert g.gemm_plan(M, N, K)["name"] == "128x128x64_w8_s4", (M, N, K)
     assert g.gemm_plan(256, 16384, 4096)["name"] == "256x128x64_w4_u8"
+    # M > 256: the 128x128 tile where its tiles fit one pass and fill it at
+    # least as well as the ping-pong tile
+    for M, N, K in ((640, 2048, 8192), (768, 4096, 4096), (384, 8192, 4096)):
+        assert g.gemm_plan(M, N, K)["name"] == "128x128x64_w8_s4", (M, N, K)
+    assert g.gemm_plan(512, 16384, 2048)["name"] == "256x256x64_w8_pp2"
     # as full as the ping-pong tile, whose two splits would hold 32 slabs each
     assert g.gemm_plan(256, 28672, 4096)["name"] == "256x128x64_w4_u8"
     # more than two splits on the ping-pong tile take the second pass
