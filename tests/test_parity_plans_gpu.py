@@ -117,3 +117,27 @@ def test_longest_k_every_element(M, N, K):
     err, worst = compare_full(C, A, B, K, "bf16", "fp32", "M=%d N=%d K=%d" % (M, N, K))
     say("  max|err|=%.3g worst/bound=%.3g" % (err, worst))
     h.close()
+
+
+# The tile choices made by how full a pass each family would be: the 128x128
+# tile for 32 < M <= 64 past one pass of 32-row tiles, for 128 < M <= 256
+# with short K or few N tiles, and above M = 256 where its tiles fit one
+# pass; the four-wave tile over the ping-pong one.  Every element against
+# the oracle, through the default plan.
+FILL_CASES = [((40, 20480, 4096), "128x128x64_w8_s4"), ((200, 6144, 3072), "128x128x64_w8_s4"),
+              ((256, 2048, 8192), "128x128x64_w8_s4"), ((640, 2048, 8192), "128x128x64_w8_s4"),
+              ((384, 4096, 2048), "128x128x64_w8_s4"), ((256, 16384, 4096), "256x128x64_w4_u8"),
+              ((256, 28672, 4096), "256x128x64_w4_u8")]
+
+
+@pytest.mark.parametrize("shape,name", FILL_CASES, ids=["%dx%dx%d" % s for s, _ in FILL_CASES])
+def test_fill_rule_plans_every_element(shape, name):
+    M, N, K = shape
+    p = gemm_plan(M, N, K, CODE["bf16"], CODE["bf16"])
+    assert p["name"] == name, p
+    say("case fill-rule plan M=%d N=%d K=%d %s splits=%d" % (M, N, K, p["name"], p["splits"]))
+    h = new_handle()
+    A, B = make_operands(M, N, K, "bf16", "llm", seed=M + N)
+    C = run_gpu(h, A, B, K, "bf16", "bf16")
+    compare_full(C, A, B, K, "bf16", "bf16", "fill rule M=%d N=%d K=%d" % (M, N, K))
+    h.close()
