@@ -2,7 +2,8 @@
 C ABI, on the GPU: its output against gemm_run's on the same inputs, on two
 calls in a row, the second with a smaller input; a shape whose default plan
 needs more partials than the scratch holds; the same bits on a split plan that
-fills the scratch; and no device allocation once the scratch is loaded."""
+fills the scratch and on small-M plans whose splits are reduced in the kernel;
+and no device allocation once the scratch is loaded."""
 import numpy as np
 import pytest
 import torch
@@ -78,6 +79,24 @@ def test_same_bits_on_a_split_plan_that_fills_the_scratch():
     C = _noalloc(A, B, K, "bf16", "bf16")
     R = run_gpu(h, A, B, K, "bf16", "bf16")
     assert np.array_equal(C, R)
+    h.close()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8192, 8192), (96, 8192, 8192), (20, 1000, 4104)])
+def test_tile_kernel_in_kernel_reduction_matches_gemm_run(M, N, K):
+    # small-M plans on the 32x128 and 128x128 tiles: K splits reduced in the
+    # kernel through the scratch's slots and counters, in the rotated slab
+    # order; the same plan as gemm_run's, so the same bits, and again on a
+    # second call (the counters are back at zero)
+    from dense_gemm_nt_amd import gemm_plan
+    p = gemm_plan(M, N, K, 0, 0)
+    assert p["splits"] > 1 and p["inreduce"] == 1, p
+    say("case noalloc tile in-kernel M=%d N=%d K=%d %s splits=%d" % (M, N, K, p["name"], p["splits"]))
+    h = new_handle()
+    A, B = make_operands(M, N, K, "bf16", "llm", seed=M)
+    R = run_gpu(h, A, B, K, "bf16", "bf16")
+    for _ in range(2):
+        assert np.array_equal(_noalloc(A, B, K, "bf16", "bf16"), R)
     h.close()
 
 
