@@ -238,18 +238,18 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
         const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
         if (cfg == CFG_PP2_256x256 && t128 < kNumCUs && fill(blocks(t128, 8)) >= fill(blocks(big, 20)))
             cfg = CFG_T128x128;
-        // Small squares: the 32x128 tile, when without K splits it fills at
-        // least as many compute units (in one pass) as the 128x128 tile does with
-        // the splits the rule below gives it; it then needs no partials.
-        if (cfg == CFG_T128x128) {
-            const int64_t t128 = cdiv(M, 128) * cdiv(N, 128), t32 = cdiv(M, 32) * cdiv(N, 128);
-            const int64_t kt = cdiv(K, 64);
-            int64_t s128 = 1;
-            if (t128 < kNumCUs && kt >= 16)
-                s128 = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / t128, kt / 8));
-            if (t32 <= kNumCUs && t32 >= t128 * s128)
-                cfg = CFG_T32x128;
-        }
+    }
+    // The 32x128 tile wherever the 128x128 tile was chosen above M = 64 but
+    // the 32-row tiles, in one pass with their own K splits, fill the machine
+    // strictly better: small squares and small problems with short K, where
+    // the 128-row tiles leave compute units idle (178 x 640 x 2240: 11.4
+    // against 16.6 us; 74 x 1408 x 512 9.3 against 11.2; 618 x 704 x 3968
+    // 16.8 against 19.8; 1024^3 and smaller squares).  On a tie the
+    // 128x128 tile, whose blocks do more work per byte staged.
+    if (cfg == CFG_T128x128 && M > 64) {
+        const int64_t t32 = cdiv(M, 32) * cdiv(N, 128), t128 = cdiv(M, 128) * cdiv(N, 128);
+        if (t32 <= kNumCUs && fill(blocks(t32, 8)) > fill(blocks(t128, 8)))
+            cfg = CFG_T32x128;
     }
     // 128x128 tiles that overflow one pass of the machine but fit two: the
     // two-stage ring (64 KB of LDS) lets two blocks share a compute unit, so

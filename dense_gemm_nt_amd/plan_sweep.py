@@ -53,6 +53,13 @@ SWEEPS = {
          (640, 2048, 8192, "bf16", "bf16", "llm"), (512, 16384, 2048, "bf16", "bf16", "llm"),
          (512, 8192, 8192, "bf16", "bf16", "llm"), (768, 8192, 2048, "bf16", "bf16", "llm")],
         [("plan", {}), (T128, {"GEMM_CONFIG": T128}), (PP2, {"GEMM_CONFIG": PP2})]),
+    "small_tile_fill": (
+        "M > 64: the 32x128 tile where the 128x128 tile was chosen but the 32-row tiles, in one "
+        "pass with their own K splits, fill the machine strictly better",
+        [(178, 640, 2240, "bf16", "bf16", "llm"), (74, 1408, 512, "bf16", "bf16", "llm"),
+         (618, 704, 3968, "bf16", "bf16", "llm"), (640, 768, 8192, "bf16", "bf16", "llm"),
+         (192, 4096, 4096, "bf16", "bf16", "llm"), (96, 8192, 8192, "bf16", "bf16", "llm")],
+        [("plan", {}), (T32, {"GEMM_CONFIG": T32}), (T128, {"GEMM_CONFIG": T128})]),
     "small_m": (
         "M <= 64: the 32x128 tile while its tiles fit one pass of the machine (M <= 32 always); "
         "from M = 96, or past one pass, the 128x128 tile",
@@ -61,8 +68,8 @@ SWEEPS = {
          (32, 28672, 8192, "bf16", "bf16", "llm"), (64, 4096, 4096, "bf16", "bf16", "llm")],
         [("plan", {}), (T32, {"GEMM_CONFIG": T32}), (T128, {"GEMM_CONFIG": T128})]),
     "small_square": (
-        "small squares: the 32x128 tile when it fills at least as many compute units "
-        "without K splits as the 128x128 tile does with them",
+        "small squares: the 32x128 tile when, in one pass with its K splits, it fills the "
+        "machine strictly better than the 128x128 tile with its splits",
         [(n, n, n, "bf16", "fp32", "uniform") for n in (512, 768, 1024, 1536, 2048)],
         [("plan", {}), (T32, {"GEMM_CONFIG": T32}), (T128, {"GEMM_CONFIG": T128}),
          (PP2, {"GEMM_CONFIG": PP2})]),

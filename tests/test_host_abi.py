@@ -157,8 +157,11 @@ def test_plan_regimes(g):
     # blocks per compute unit when its tiles overflow one pass of the machine
     assert g.gemm_plan(1000, 4097, 1536)["name"] == "128x128x64_w8_s2"
     assert g.gemm_plan(1000, 4096, 1536)["name"] == "128x128x64_w8_s4"
-    # small squares: four times the blocks of the 32x128 tile, unless the
-    # 128x128 tile with K splits fills as many compute units
+    # the 32x128 tile where, in one pass with its own splits, it fills the
+    # machine strictly better than the 128x128 tile (small squares, small
+    # problems with short K); on a tie the 128x128 tile
+    for M, N, K in ((178, 640, 2240), (74, 1408, 512), (618, 704, 3968)):
+        assert g.gemm_plan(M, N, K)["name"] == "32x128x64_w4_s6", (M, N, K)
     assert g.gemm_plan(512, 512, 512)["name"] == "32x128x64_w4_s6"
     assert g.gemm_plan(1024, 1024, 1024)["name"] == "32x128x64_w4_s6"
     assert g.gemm_plan(640, 768, 8192)["name"] == "128x128x64_w8_s4"
