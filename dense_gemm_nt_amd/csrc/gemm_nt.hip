@@ -241,11 +241,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int force_cfg,
     }
     // The 32x128 tile wherever the 128x128 tile was chosen above M = 64 but
     // the 32-row tiles, in one pass with their own K splits, fill the machine
-    // strictly better: small squares and small problems with short K, where
-    // the 128-row tiles leave compute units idle (178 x 640 x 2240: 11.4
-    // against 16.6 us; 74 x 1408 x 512 9.3 against 11.2; 618 x 704 x 3968
-    // 16.8 against 19.8; 1024^3 and smaller squares).  On a tie the
-    // 128x128 tile, whose blocks do more work per byte staged.
+    // strictly better: small squares and small problems with short K.  On
+    // the small ragged shapes it takes, the two tiles, each with its own K
+    // splits, measured level (178 x 640 x 2240: 11.0 us both; 74 x 1408 x
+    // 512 8.8; 618 x 704 x 3968 16.4 against 16.3), where the plans that
+    // earlier rules made for them took 16.6, 11.2 and 19.8 us.  On a tie
+    // the 128x128 tile, whose blocks do more work per byte staged.
     if (cfg == CFG_T128x128 && M > 64) {
         const int64_t t32 = cdiv(M, 32) * cdiv(N, 128), t128 = cdiv(M, 128) * cdiv(N, 128);
         if (t32 <= kNumCUs && fill(blocks(t32, 8)) > fill(blocks(t128, 8)))
