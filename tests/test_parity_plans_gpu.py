@@ -127,7 +127,12 @@ def test_longest_k_every_element(M, N, K):
 FILL_CASES = [((40, 20480, 4096), "128x128x64_w8_s4"), ((200, 6144, 3072), "128x128x64_w8_s4"),
               ((256, 2048, 8192), "128x128x64_w8_s4"), ((640, 2048, 8192), "128x128x64_w8_s4"),
               ((384, 4096, 2048), "128x128x64_w8_s4"), ((256, 16384, 4096), "256x128x64_w4_u8"),
-              ((256, 28672, 4096), "256x128x64_w4_u8")]
+              ((256, 28672, 4096), "256x128x64_w4_u8"),
+              # above M = 64, the 32x128 tile where its tiles fill one pass
+              # strictly better (M not a multiple of 32 on all three, N not a
+              # multiple of 128 on the last)
+              ((178, 640, 2240), "32x128x64_w4_s6"), ((74, 1408, 512), "32x128x64_w4_s6"),
+              ((618, 704, 3968), "32x128x64_w4_s6")]
 
 
 @pytest.mark.parametrize("shape,name", FILL_CASES, ids=["%dx%dx%d" % s for s, _ in FILL_CASES])
